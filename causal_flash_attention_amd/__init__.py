@@ -1,0 +1,22 @@
+"""Causal multi-head self-attention (FlashAttention style) for MI355X / gfx950.
+
+The computation lives in the HIP library ``libcausal_attn.so`` (C ABI in
+``include/causal_attn.h``); this package is its Python binding. Importing the
+package does not load the library; the first call does, and fails loudly if
+the library has not been built.
+"""
+
+from .binding import (  # noqa: F401
+    AttnError,
+    attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
+    attn_bwd_preprocess,
+    attn_fwd,
+    attn_last_error,
+    attn_status_string,
+    attn_version,
+    backward,
+    forward,
+    lib,
+)

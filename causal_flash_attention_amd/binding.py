@@ -1,0 +1,225 @@
+"""Python binding of libcausal_attn.so (ctypes, argument marshalling only).
+
+The functions named like the C ABI (``attn_fwd``, ``attn_bwd``, ...) take
+torch tensors that already live on the GPU, check dtype / shape / device /
+contiguity, pass raw pointers and the current HIP stream to the library and
+raise :class:`AttnError` on a non-zero status. Every step of the computation
+runs in the library's HIP kernels; there is no fallback. ``forward`` and
+``backward`` additionally allocate their outputs with torch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+from .build import LIB_PATH
+
+ATTN_OK = 0
+STATUS_NAMES = {
+    0: "ATTN_OK",
+    -1: "ATTN_ERR_NULL_PTR",
+    -2: "ATTN_ERR_BAD_SHAPE",
+    -3: "ATTN_ERR_UNSUPPORTED",
+    -4: "ATTN_ERR_TOO_LARGE",
+    -5: "ATTN_ERR_MISALIGNED",
+    -6: "ATTN_ERR_ALIAS",
+    -7: "ATTN_ERR_HIP",
+}
+
+# Every symbol include/causal_attn.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_preprocess": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_dkdv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_dq": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_status_string": ([_I], ctypes.c_char_p),
+    "attn_last_error": ([], ctypes.c_char_p),
+    "attn_version": ([], _I),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str = ""):
+        self.status = status
+        name = STATUS_NAMES.get(status, f"status {status}")
+        super().__init__(f"{func}: {name}" + (f" ({detail})" if detail else ""))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m causal_flash_attention_amd.build` (hipcc, gfx950)")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = handle
+    return _lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != ATTN_OK:
+        detail = lib().attn_last_error().decode(errors="replace")
+        raise AttnError(status, func, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else 0
+
+
+def _require(t, name: str, dtype, shape) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(qkv, n_head: int, head_dim: int) -> Tuple[int, int, int]:
+    if qkv.dim() != 3 or qkv.shape[2] != 3 * n_head * head_dim:
+        raise ValueError("qkv must be (B, T, 3 * n_head * head_dim)")
+    return int(qkv.shape[0]), int(qkv.shape[1]), n_head * head_dim
+
+
+def _elem(qkv):
+    torch = _torch()
+    if qkv.dtype == torch.bfloat16:
+        return torch.bfloat16, ""
+    if qkv.dtype == torch.float32:
+        return torch.float32, "_f32"
+    raise ValueError("qkv must be bfloat16 or float32")
+
+
+# ---------------------------------------------------------------------------
+# Same-named wrappers of the C entry points.
+# ---------------------------------------------------------------------------
+
+def attn_fwd(qkv, out, lse, n_head: int, head_dim: int = 64, stream=None) -> None:
+    torch = _torch()
+    dt, sfx = _elem(qkv)
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(qkv, "qkv", dt, (B, T, 3 * C))
+    _require(out, "out", dt, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    fn = getattr(lib(), "attn_fwd" + sfx)
+    _check(fn(_ptr(qkv), _ptr(out), _ptr(lse), B, T, n_head, head_dim, _stream_ptr(stream)),
+           "attn_fwd" + sfx)
+
+
+def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
+             stream=None) -> None:
+    torch = _torch()
+    dt, sfx = _elem(qkv)
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(dout, "dout", dt, (B, T, C))
+    _require(qkv, "qkv", dt, (B, T, 3 * C))
+    _require(out, "out", dt, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require(dqkv, "dqkv", dt, (B, T, 3 * C))
+    _require(delta, "delta", torch.float32, (B, n_head, T))
+    fn = getattr(lib(), "attn_bwd" + sfx)
+    _check(fn(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dqkv), _ptr(delta),
+              B, T, n_head, head_dim, _stream_ptr(stream)), "attn_bwd" + sfx)
+
+
+def attn_bwd_preprocess(dout, out, delta, n_head: int, head_dim: int = 64, stream=None) -> None:
+    torch = _torch()
+    B, T, C = int(out.shape[0]), int(out.shape[1]), n_head * head_dim
+    _require(out, "out", torch.bfloat16, (B, T, C))
+    _require(dout, "dout", torch.bfloat16, (B, T, C))
+    _require(delta, "delta", torch.float32, (B, n_head, T))
+    _check(lib().attn_bwd_preprocess(_ptr(dout), _ptr(out), _ptr(delta), B, T, n_head, head_dim,
+                                     _stream_ptr(stream)), "attn_bwd_preprocess")
+
+
+def _bwd_stage(name, dout, qkv, lse, delta, dqkv, n_head, head_dim, stream):
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _require(dout, "dout", torch.bfloat16, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require(delta, "delta", torch.float32, (B, n_head, T))
+    _require(dqkv, "dqkv", torch.bfloat16, (B, T, 3 * C))
+    _check(getattr(lib(), name)(_ptr(dout), _ptr(qkv), _ptr(lse), _ptr(delta), _ptr(dqkv),
+                                B, T, n_head, head_dim, _stream_ptr(stream)), name)
+
+
+def attn_bwd_dkdv(dout, qkv, lse, delta, dqkv, n_head: int, head_dim: int = 64,
+                  stream=None) -> None:
+    _bwd_stage("attn_bwd_dkdv", dout, qkv, lse, delta, dqkv, n_head, head_dim, stream)
+
+
+def attn_bwd_dq(dout, qkv, lse, delta, dqkv, n_head: int, head_dim: int = 64,
+                stream=None) -> None:
+    _bwd_stage("attn_bwd_dq", dout, qkv, lse, delta, dqkv, n_head, head_dim, stream)
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(status).decode()
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode(errors="replace")
+
+
+def attn_version() -> int:
+    return int(lib().attn_version())
+
+
+# ---------------------------------------------------------------------------
+# Allocating conveniences.
+# ---------------------------------------------------------------------------
+
+def forward(qkv, n_head: int, head_dim: int = 64, stream=None):
+    """Returns (out, lse) for a packed (B, T, 3C) bf16 or fp32 GPU tensor."""
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+    attn_fwd(qkv, out, lse, n_head, head_dim, stream)
+    return out, lse
+
+
+def backward(dout, qkv, out, lse, n_head: int, head_dim: int = 64, stream=None):
+    """Returns dqkv (B, T, 3C) for the forward that produced (out, lse)."""
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    dqkv = torch.empty_like(qkv)
+    delta = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+    attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
+    return dqkv

@@ -1,0 +1,267 @@
+// C ABI of the causal attention library: argument checks, then kernel
+// launches on the caller's stream. Declared in include/causal_attn.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "causal_attn.h"
+
+namespace cattn {
+hipError_t launch_attn_fwd_bf16(const void*, void*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_pre_bf16(const void*, const void*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, const float*, void*,
+                                     int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dq_bf16(const void*, const void*, const float*, const float*, void*,
+                                   int, int, int, hipStream_t);
+hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_pre_f32(const float*, const float*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dkdv_f32(const float*, const float*, const float*, const float*, float*,
+                                    int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dq_f32(const float*, const float*, const float*, const float*, float*,
+                                  int, int, int, hipStream_t);
+}  // namespace cattn
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kHeadDim = 64;
+constexpr long long kMaxBytes = 1LL << 62;
+constexpr long long kMaxBlocks = 0x7fffffffLL;
+
+thread_local char g_last_error[256];
+
+int fail(int status, const char* what) {
+    snprintf(g_last_error, sizeof g_last_error, "%s", what);
+    return status;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+    return ATTN_ERR_HIP;
+}
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+    const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shape checks shared by every entry point. Sets *empty when there is
+// nothing to compute.
+int check_shape(int B, int T, int H, int d, int elem, bool* empty) {
+    if (B < 0 || T < 0 || H < 0 || d <= 0) return fail(ATTN_ERR_BAD_SHAPE, "B, T, n_head must be >= 0 and head_dim > 0");
+    if (d != kHeadDim) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64");
+    *empty = (B == 0 || T == 0 || H == 0);
+    if (*empty) return ATTN_OK;
+    // Largest tensor: qkv / dqkv with B*T*3*H*d elements; grid: B*H*ceil(T/64).
+    const long long bt = (long long)B * T;
+    const long long c3 = 3LL * H * d;
+    if (bt > kMaxBytes / c3 / elem) return fail(ATTN_ERR_TOO_LARGE, "B*T*3*n_head*head_dim overflows");
+    const long long blocks = (long long)B * H * ((T + 63) / 64);
+    if (blocks > kMaxBlocks) return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
+    // the preprocess grid: 16 rows of (b, t, h) per workgroup in float32
+    if (((long long)B * T * H + 15) / 16 > kMaxBlocks)
+        return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
+    if ((long long)H * d > 0x7fffffffLL / 3) return fail(ATTN_ERR_TOO_LARGE, "3*n_head*head_dim overflows int");
+    return ATTN_OK;
+}
+
+int check_aligned(const void* p, uintptr_t a, const char* name) {
+    if (reinterpret_cast<uintptr_t>(p) % a != 0) return fail(ATTN_ERR_MISALIGNED, name);
+    return ATTN_OK;
+}
+
+// Outputs may not overlap any input or any other output.
+int check_disjoint(const Span* outs, int n_out, const Span* ins, int n_in) {
+    thread_local char msg[128];
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlaps(outs[i], ins[j])) {
+                snprintf(msg, sizeof msg, "%s overlaps %s", outs[i].name, ins[j].name);
+                return fail(ATTN_ERR_ALIAS, msg);
+            }
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j])) {
+                snprintf(msg, sizeof msg, "%s overlaps %s", outs[i].name, outs[j].name);
+                return fail(ATTN_ERR_ALIAS, msg);
+            }
+    }
+    return ATTN_OK;
+}
+
+Span span(const void* p, long long bytes, const char* name) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + (uintptr_t)bytes, name};
+}
+
+struct Sizes {
+    long long qkv, bt_c, rows;  // bytes of qkv, bytes of a (B,T,C) tensor, bytes of (B,H,T) fp32
+};
+
+Sizes sizes(int B, int T, int H, int elem) {
+    const long long n = (long long)B * T * H * kHeadDim;
+    return Sizes{3 * n * elem, n * elem, (long long)B * H * T * 4};
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int fwd_common(const void* qkv, void* out, float* lse, int B, int T, int H, int d, void* stream,
+               int elem) {
+    g_last_error[0] = '\0';
+    bool empty = false;
+    if (!(B == 0 || T == 0 || H == 0) && (!qkv || !out || !lse))
+        return fail(ATTN_ERR_NULL_PTR, !qkv ? "qkv is NULL" : !out ? "out is NULL" : "lse is NULL");
+    int st = check_shape(B, T, H, d, elem, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_aligned(qkv, 16, "qkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(out, 16, "out must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, elem);
+    const Span ins[] = {span(qkv, z.qkv, "qkv")};
+    const Span outs[] = {span(out, z.bt_c, "out"), span(lse, z.rows, "lse")};
+    if ((st = check_disjoint(outs, 2, ins, 1)) != ATTN_OK) return st;
+    hipError_t e = elem == 2
+        ? cattn::launch_attn_fwd_bf16(qkv, out, lse, B, T, H, as_stream(stream))
+        : cattn::launch_attn_fwd_f32(static_cast<const float*>(qkv), static_cast<float*>(out), lse,
+                                     B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_fwd launch");
+}
+
+enum Stage { kPre = 1, kDkdv = 2, kDq = 4, kAll = 7 };
+
+int bwd_common(const void* dout, const void* qkv, const void* out, const float* lse, void* dqkv,
+               float* delta, int B, int T, int H, int d, void* stream, int elem, int stages) {
+    g_last_error[0] = '\0';
+    const bool nonempty = !(B == 0 || T == 0 || H == 0);
+    if (nonempty) {
+        if (!dout) return fail(ATTN_ERR_NULL_PTR, "dout is NULL");
+        if ((stages & (kDkdv | kDq)) && !qkv) return fail(ATTN_ERR_NULL_PTR, "qkv is NULL");
+        if ((stages & kPre) && !out) return fail(ATTN_ERR_NULL_PTR, "out is NULL");
+        if ((stages & (kDkdv | kDq)) && !lse) return fail(ATTN_ERR_NULL_PTR, "lse is NULL");
+        if ((stages & (kDkdv | kDq)) && !dqkv) return fail(ATTN_ERR_NULL_PTR, "dqkv is NULL");
+        if (!delta) return fail(ATTN_ERR_NULL_PTR, "delta is NULL");
+    }
+    bool empty = false;
+    int st = check_shape(B, T, H, d, elem, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_aligned(dout, 16, "dout must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((stages & (kDkdv | kDq)) && (st = check_aligned(qkv, 16, "qkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((stages & kPre) && (st = check_aligned(out, 16, "out must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((stages & (kDkdv | kDq)) && (st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    if ((stages & (kDkdv | kDq)) && (st = check_aligned(dqkv, 16, "dqkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(delta, 4, "delta must be 4-byte aligned")) != ATTN_OK) return st;
+
+    const Sizes z = sizes(B, T, H, elem);
+    Span ins[4];
+    int n_in = 0;
+    ins[n_in++] = span(dout, z.bt_c, "dout");
+    if (stages & (kDkdv | kDq)) {
+        ins[n_in++] = span(qkv, z.qkv, "qkv");
+        ins[n_in++] = span(lse, z.rows, "lse");
+    }
+    if (stages & kPre) ins[n_in++] = span(out, z.bt_c, "out");
+    Span outs[2];
+    int n_out = 0;
+    if (stages & (kDkdv | kDq)) outs[n_out++] = span(dqkv, z.qkv, "dqkv");
+    // delta is written by the preprocess stage and read by the others.
+    if (stages & kPre) outs[n_out++] = span(delta, z.rows, "delta");
+    else ins[n_in++] = span(delta, z.rows, "delta");
+    if ((st = check_disjoint(outs, n_out, ins, n_in)) != ATTN_OK) return st;
+
+    const hipStream_t s = as_stream(stream);
+    hipError_t e = hipSuccess;
+    if (elem == 2) {
+        if (stages & kPre) {
+            e = cattn::launch_attn_bwd_pre_bf16(dout, out, delta, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd preprocess launch");
+        }
+        if (stages & kDkdv) {
+            e = cattn::launch_attn_bwd_dkdv_bf16(qkv, dout, lse, delta, dqkv, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd dK/dV launch");
+        }
+        if (stages & kDq) {
+            e = cattn::launch_attn_bwd_dq_bf16(qkv, dout, lse, delta, dqkv, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd dQ launch");
+        }
+    } else {
+        const float* f_dout = static_cast<const float*>(dout);
+        const float* f_qkv = static_cast<const float*>(qkv);
+        float* f_dqkv = static_cast<float*>(dqkv);
+        if (stages & kPre) {
+            e = cattn::launch_attn_bwd_pre_f32(f_dout, static_cast<const float*>(out), delta, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 preprocess launch");
+        }
+        if (stages & kDkdv) {
+            e = cattn::launch_attn_bwd_dkdv_f32(f_qkv, f_dout, lse, delta, f_dqkv, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 dK/dV launch");
+        }
+        if (stages & kDq) {
+            e = cattn::launch_attn_bwd_dq_f32(f_qkv, f_dout, lse, delta, f_dqkv, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 dQ launch");
+        }
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* qkv, void* out, float* lse, int B, int T, int n_head, int head_dim,
+             void* stream) {
+    return fwd_common(qkv, out, lse, B, T, n_head, head_dim, stream, 2);
+}
+
+int attn_bwd(const void* dout, const void* qkv, const void* out, const float* lse, void* dqkv,
+             float* delta, int B, int T, int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, out, lse, dqkv, delta, B, T, n_head, head_dim, stream, 2, kAll);
+}
+
+int attn_bwd_preprocess(const void* dout, const void* out, float* delta, int B, int T, int n_head,
+                        int head_dim, void* stream) {
+    return bwd_common(dout, nullptr, out, nullptr, nullptr, delta, B, T, n_head, head_dim, stream,
+                      2, kPre);
+}
+
+int attn_bwd_dkdv(const void* dout, const void* qkv, const float* lse, const float* delta,
+                  void* dqkv, int B, int T, int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, nullptr, lse, dqkv, const_cast<float*>(delta), B, T, n_head,
+                      head_dim, stream, 2, kDkdv);
+}
+
+int attn_bwd_dq(const void* dout, const void* qkv, const float* lse, const float* delta,
+                void* dqkv, int B, int T, int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, nullptr, lse, dqkv, const_cast<float*>(delta), B, T, n_head,
+                      head_dim, stream, 2, kDq);
+}
+
+int attn_fwd_f32(const float* qkv, float* out, float* lse, int B, int T, int n_head, int head_dim,
+                 void* stream) {
+    return fwd_common(qkv, out, lse, B, T, n_head, head_dim, stream, 4);
+}
+
+int attn_bwd_f32(const float* dout, const float* qkv, const float* out, const float* lse,
+                 float* dqkv, float* delta, int B, int T, int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, out, lse, dqkv, delta, B, T, n_head, head_dim, stream, 4, kAll);
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_NULL_PTR: return "ATTN_ERR_NULL_PTR";
+        case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_TOO_LARGE: return "ATTN_ERR_TOO_LARGE";
+        case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED";
+        case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+        default: return "ATTN_ERR_UNKNOWN";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_version(void) { return kVersion; }
+
+}  // extern "C"

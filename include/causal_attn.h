@@ -1,0 +1,135 @@
+/*
+ * causal_attn.h -- C ABI of the MI355X (gfx950) causal multi-head
+ * self-attention library, forward and backward, FlashAttention style.
+ *
+ * The operation (the plain definition the kernels reproduce, up to rounding):
+ * for every batch row b and head h, with Q, K, V the (T, d) slices of the
+ * packed qkv tensor and scale = 1/sqrt(d),
+ *
+ *     S = scale * Q K^T, masked to -inf where key j > query i
+ *     P = row softmax of S,   O = P V,   LSE[i] = ln sum_j exp(S[i, j])
+ *
+ * and, for an upstream gradient G = dL/dO,
+ *
+ *     D[i] = sum_k G[i, k] O[i, k],   dS = P * (G V^T - D)
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T G.
+ *
+ * Source: flash attention is attention computed without ever keeping the full
+ * T x T attention matrix in GPU memory, used in every training step of GPT-2
+ * (theprofessional.online summary of "Let's reproduce GPT-2 (124M)",
+ * glossary table, row "flash attention"; "Andrej Karpathy - Lets reproduce
+ * GPT 2 124M", chapter list, 02:00:18); the model predicts the next token,
+ * so the attention is causal (same glossary, row "loss"); the formula is the
+ * scaled dot-product attention of "Attention is All You Need", linked from
+ * the same chapter list. The pages give no equations: the mask includes the
+ * diagonal, the scale is fixed at 1/sqrt(head_dim) and LSE is the natural
+ * log of the sum over the scaled logits.
+ *
+ * Layouts (all contiguous, row-major, C = n_head * head_dim):
+ *   qkv   (B, T, 3C)  [Q | K | V] along the last axis; head h occupies
+ *                     columns h*d .. h*d+d-1 of each of the three blocks
+ *   out   (B, T, C)   same head placement as one block of qkv
+ *   lse   (B, n_head, T) float32
+ *   dout  (B, T, C)   gradient of the loss with respect to out
+ *   dqkv  (B, T, 3C)  [dQ | dK | dV], mirrors qkv; overwritten, never
+ *                     accumulated into
+ *   delta (B, n_head, T) float32 workspace; on return from attn_bwd (once
+ *                     the stream has run) it holds D
+ * Element types: the unsuffixed calls take bf16 (IEEE binary32 upper half,
+ * passed as void*), accumulate in float32 and round results to nearest-even
+ * bf16; the _f32 calls take and produce float32 throughout.
+ *
+ * Ownership and synchronisation: every pointer is device memory owned by the
+ * caller. The library never allocates, frees or synchronises: each call
+ * validates its arguments, enqueues its kernels on `stream` (a hipStream_t
+ * passed as void*; NULL is the default stream) and returns. ATTN_OK means
+ * "validated and enqueued"; a fault inside a kernel surfaces at the caller's
+ * next synchronisation. The library holds no state, so calls on different
+ * streams may run concurrently as long as their buffers do not overlap.
+ *
+ * Shapes: head_dim must be 64. B, T and n_head may be any non-negative value
+ * whose tensors fit in 2^62 bytes; a call with B, T or n_head equal to 0 has
+ * nothing to compute and returns ATTN_OK without touching memory (its
+ * pointers may then be NULL). bf16 tensors (qkv, out, dout, dqkv) must start
+ * on a 16-byte boundary, float32 tensors on a 4-byte boundary (16 bytes for
+ * qkv, out, dout and dqkv of the _f32 calls). Outputs may not overlap inputs
+ * or each other.
+ *
+ * Errors: every call returns a status code and never throws. Argument checks
+ * run before any HIP call, in this order: NULL pointer, shape, unsupported
+ * head_dim, size overflow, alignment, overlap.
+ */
+#ifndef CAUSAL_ATTN_H
+#define CAUSAL_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_PTR = -1,     /* a required pointer is NULL */
+    ATTN_ERR_BAD_SHAPE = -2,    /* B, T or n_head negative, head_dim <= 0 */
+    ATTN_ERR_UNSUPPORTED = -3,  /* head_dim other than 64 */
+    ATTN_ERR_TOO_LARGE = -4,    /* a tensor or the launch grid would overflow */
+    ATTN_ERR_MISALIGNED = -5,   /* a pointer is not aligned as required */
+    ATTN_ERR_ALIAS = -6,        /* an output overlaps an input or another output */
+    ATTN_ERR_HIP = -7           /* the HIP runtime refused a launch */
+};
+
+/* ---------------------------------------------------------------- bf16 ---- */
+
+/* Forward: out = attention(qkv), lse = per-row log-sum-exp. One kernel. */
+int attn_fwd(const void* qkv, void* out, float* lse,
+             int B, int T, int n_head, int head_dim, void* stream);
+
+/* Backward: dqkv = gradients of sum(dout * out) with respect to qkv, given
+ * the out and lse written by attn_fwd for the same qkv. Runs
+ * attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq in that order on
+ * `stream`; `delta` is the caller's (B, n_head, T) float32 workspace. */
+int attn_bwd(const void* dout, const void* qkv, const void* out,
+             const float* lse, void* dqkv, float* delta,
+             int B, int T, int n_head, int head_dim, void* stream);
+
+/* The three stages of attn_bwd, exported so that each kernel can be launched
+ * and timed on its own.
+ *   attn_bwd_preprocess: delta[b,h,t] = sum_k dout[b,t,h,k] * out[b,t,h,k]
+ *   attn_bwd_dkdv:       writes the dK and dV blocks of dqkv
+ *   attn_bwd_dq:         writes the dQ block of dqkv
+ * dkdv and dq read delta, so they must follow preprocess on the stream;
+ * they write disjoint columns of dqkv and may run in either order. */
+int attn_bwd_preprocess(const void* dout, const void* out, float* delta,
+                        int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_dkdv(const void* dout, const void* qkv, const float* lse,
+                  const float* delta, void* dqkv,
+                  int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_dq(const void* dout, const void* qkv, const float* lse,
+                const float* delta, void* dqkv,
+                int B, int T, int n_head, int head_dim, void* stream);
+
+/* --------------------------------------------------------------- fp32 ---- */
+
+/* Same operations in float32 storage and arithmetic. */
+int attn_fwd_f32(const float* qkv, float* out, float* lse,
+                 int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_f32(const float* dout, const float* qkv, const float* out,
+                 const float* lse, float* dqkv, float* delta,
+                 int B, int T, int n_head, int head_dim, void* stream);
+
+/* ------------------------------------------------------------- status ---- */
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Detail of the last failing call on the calling thread (argument name or
+ * HIP error text); "" if none. Valid until the thread's next library call. */
+const char* attn_last_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ATTN_H */

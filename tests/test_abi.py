@@ -1,0 +1,156 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+declared symbol, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_flash_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "causal_attn.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Fake device addresses are passed below only to calls whose validation must
+# fail before any launch; never run them where a GPU could execute a kernel.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="uses fake device addresses")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("library not built")
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
+              "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "attn_last_error",
+              "attn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(binding.SIGNATURES)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in binding.STATUS_NAMES.items():
+        assert L.attn_status_string(code).decode() == name
+    assert L.attn_status_string(12345).decode() == "ATTN_ERR_UNKNOWN"
+    assert L.attn_version() == 10000
+
+
+Q, O, LS, G, DQ, DL = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_f32"])
+def test_forward_validation(L, fn):
+    f = getattr(L, fn)
+    ok = (1, 64, 2, 64)
+    assert f(None, O, LS, *ok, None) == -1
+    assert f(Q, None, LS, *ok, None) == -1
+    assert f(Q, O, None, *ok, None) == -1
+    assert f(Q, O, LS, -1, 64, 2, 64, None) == -2
+    assert f(Q, O, LS, 1, -5, 2, 64, None) == -2
+    assert f(Q, O, LS, 1, 64, -2, 64, None) == -2
+    assert f(Q, O, LS, 1, 64, 2, 0, None) == -2
+    assert f(Q, O, LS, 1, 64, 2, 128, None) == -3
+    assert f(Q, O, LS, 1, 64, 2, 32, None) == -3
+    assert f(Q, O, LS, 2**31 - 1, 2**31 - 1, 2**20, 64, None) == -4
+    assert f(Q, O, LS, 1, 2**31 - 1, 2**20, 64, None) == -4
+    assert f(Q + 8, O, LS, *ok, None) == -5
+    assert f(Q, O + 4, LS, *ok, None) == -5
+    assert f(Q, O, LS + 2, *ok, None) == -5
+    assert f(Q, Q + 16, LS, *ok, None) == -6   # out inside qkv
+    assert f(Q, O, O + 16, *ok, None) == -6     # lse inside out
+    assert f(Q, O, Q - 4, *ok, None) == -6      # lse runs into qkv
+    assert "overlaps" in L.attn_last_error().decode()
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", ["attn_bwd", "attn_bwd_f32"])
+def test_backward_validation(L, fn):
+    f = getattr(L, fn)
+    ok = (1, 64, 2, 64)
+    args = [G, Q, O, LS, DQ, DL]
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert f(*a, *ok, None) == -1, i
+    assert f(*args, 1, 64, 2, 63, None) == -3
+    assert f(*args, 0 - 1, 64, 2, 64, None) == -2
+    assert f(G + 4, Q, O, LS, DQ, DL, *ok, None) == -5
+    assert f(G, Q, O, LS, DQ + 2, DL, *ok, None) == -5
+    assert f(G, Q, O, LS, Q, DL, *ok, None) == -6      # dqkv aliases qkv
+    assert f(G, Q, O, LS, DQ, LS, *ok, None) == -6     # delta aliases lse
+    assert f(G, Q, O, LS, DQ, DQ + 64, *ok, None) == -6  # delta inside dqkv
+
+
+@no_gpu_only
+def test_stage_validation(L):
+    ok = (1, 64, 2, 64)
+    assert L.attn_bwd_preprocess(G, O, None, *ok, None) == -1
+    assert L.attn_bwd_preprocess(G, O, O, *ok, None) == -6
+    assert L.attn_bwd_dkdv(G, Q, LS, DL, None, *ok, None) == -1
+    assert L.attn_bwd_dkdv(G, Q, LS, DL, DQ, 1, 64, 2, 16, None) == -3
+    assert L.attn_bwd_dq(G, Q, LS, DL, Q, *ok, None) == -6
+    assert L.attn_bwd_dq(G, Q, LS, DQ + 32, DQ, *ok, None) == -6  # delta read inside dqkv
+
+
+def test_empty_problems_are_noops(L):
+    for B, T, H in ((0, 64, 2), (1, 0, 2), (1, 64, 0)):
+        assert L.attn_fwd(None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_fwd_f32(None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd(None, None, None, None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd_f32(None, None, None, None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd_dkdv(None, None, None, None, None, B, T, H, 64, None) == 0
+
+
+@no_gpu_only
+def test_launch_without_device_reports_hip_error(L):
+    # Valid arguments on a machine with no GPU: the launch itself fails and
+    # the call reports it instead of crashing.
+    assert L.attn_fwd(Q, O, LS, 1, 64, 2, 64, None) == -7
+    assert "attn_fwd" in L.attn_last_error().decode()
+    assert L.attn_bwd(G, Q, O, LS, DQ, DL, 1, 64, 2, 64, None) == -7
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+
+
+def test_binding_argument_checks_on_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    qkv = torch.zeros(1, 4, 3 * 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.attn_fwd(qkv, torch.zeros(1, 4, 64, dtype=torch.bfloat16),
+                         torch.zeros(1, 1, 4), n_head=1)
+    with pytest.raises(ValueError):
+        binding.forward(torch.zeros(1, 4, 100, dtype=torch.bfloat16), n_head=1)
+    with pytest.raises(ValueError):
+        binding.forward(torch.zeros(1, 4, 192, dtype=torch.float16), n_head=1)

@@ -1,0 +1,95 @@
+"""Parity of the HIP library against the CPU float64 oracle (needs a GPU).
+
+Inputs come from the seeded generator; both sides see identical values. The
+library is called through its C ABI (ctypes binding) with the same entry
+points and launch configuration the bench times.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from causal_flash_attention_amd import inputs as I
+from causal_flash_attention_amd.workloads import WORKLOADS
+
+from helpers import assert_parity, compare, log, run_library, sample_heads, to_device, to_host64
+
+pytestmark = pytest.mark.gpu
+
+D = 64
+
+
+def _scale_qk(qkv, dtype, H, gain):
+    """Multiply the Q and K blocks by a power of two (exact in bf16 and f32)."""
+    C = H * D
+    x = I.bf16_bits_to_f32(qkv) if dtype == "bf16" else qkv.copy()
+    x[..., :2 * C] *= np.float32(gain)
+    return I.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", qk_gain=1.0):
+    log(f"[case] {label} B={B} T={T} H={H} dtype={dtype} seed={seed} qk_gain={qk_gain}")
+    qkv, dout = I.attention_inputs(B, T, H, D, dtype, qkv_std, dout_std, seed=seed)
+    if qk_gain != 1.0:
+        qkv = _scale_qk(qkv, dtype, H, qk_gain)
+    q64, g64 = I.to_float64(qkv, dtype), I.to_float64(dout, dtype)
+    qd, gd = to_device(qkv, dtype), to_device(dout, dtype)
+    out, lse, dqkv = run_library(qd, gd, H)
+    gpu = {"out": to_host64(out), "lse": to_host64(lse), "dqkv": to_host64(dqkv)}
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    ref_out, ref_lse = oracle.forward_packed(q64, H, D, heads=heads)
+    ref_dqkv = oracle.backward_packed(g64, q64, H, D, heads=heads)
+    ref = {"out": ref_out, "lse": ref_lse, "dqkv": ref_dqkv}
+    m = compare(gpu, ref, heads, H, D)
+    for k in ("out", "lse", "dqkv"):
+        assert np.all(np.isfinite(gpu[k])), (label, k)
+    assert_parity(m, dtype, f"{label} B={B} T={T} H={H} {dtype}")
+    return m
+
+
+# ----------------------------------------------------------------------------
+# The five workloads at full size.
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_workload_parity(w):
+    if w.dtype == "f32" or w.name == "gpt2_124m_b16_t1024":
+        heads = None  # every head
+    else:
+        heads = sample_heads(w.B, w.n_head, 40, seed=1)
+    _check_case(w.B, w.T, w.n_head, w.dtype, w.qkv_std, w.dout_std, seed=0,
+                heads=heads, label=w.name)
+
+
+# ----------------------------------------------------------------------------
+# Edge shapes: T = 1, tiles +- 1, ragged tails, odd head counts.
+# ----------------------------------------------------------------------------
+
+BF16_EDGES = [(1, 1, 1), (1, 2, 1), (1, 3, 2), (1, 63, 1), (1, 64, 2), (1, 65, 1),
+              (2, 127, 3), (1, 128, 1), (3, 129, 2), (1, 191, 1), (1, 1000, 2), (2, 257, 25)]
+F32_EDGES = [(1, 1, 1), (1, 2, 2), (1, 63, 1), (1, 65, 1), (2, 129, 3), (1, 300, 2)]
+
+
+@pytest.mark.parametrize("B,T,H", BF16_EDGES)
+def test_edge_shapes_bf16(B, T, H):
+    _check_case(B, T, H, "bf16", 1.0, 0.01, seed=T, label="edge")
+
+
+@pytest.mark.parametrize("B,T,H", F32_EDGES)
+def test_edge_shapes_f32(B, T, H):
+    _check_case(B, T, H, "f32", 1.0, 1.0, seed=T, label="edge")
+
+
+def test_long_sequence_bf16():
+    _check_case(1, 4096, 2, "bf16", 1.0, 0.01, seed=7, label="long")
+
+
+def test_peaky_scores_bf16():
+    # Q and K scaled by 4: logits with a standard deviation of 16, so the
+    # running max moves often and most probabilities underflow.
+    _check_case(2, 300, 2, "bf16", 1.0, 0.01, seed=11, label="peaky", qk_gain=4.0)
+
+
+def test_peaky_scores_f32():
+    _check_case(1, 200, 2, "f32", 1.0, 1.0, seed=12, label="peaky", qk_gain=4.0)
