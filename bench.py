@@ -1,0 +1,265 @@
+"""Throughput of causal attention forward + backward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: attn_fwd then attn_bwd, on one HIP stream. W untimed
+steps, then K timed steps between two device synchronisations (HIP events on
+that stream bracket the K steps). A second timed pass of K steps launches the
+same kernels through the backward's three stage entry points
+(attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq: exactly what attn_bwd
+launches) with HIP events recorded on the stream between them, which gives
+each kernel's average duration without slowing the first pass.
+
+Prints one JSON line. ``value`` is the counted causal FLOP rate of the whole
+step (forward 2*B*H*T^2*d, backward 2.5 times that); ``roofline`` describes
+the kernel with the longest average duration; ``cpu_baseline`` is the float64
+CPU oracle timed on a bounded sample of heads of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attention fwd+bwd TFLOP/s at GPT-2 124M shape; % of bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD specification
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD specification
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "causal_flash_attention_amd", "csrc")
+
+# Kernel -> (source file, bound, algorithmic FLOPs per launch in units of one
+# causal T x T x d product per head, i.e. B*H*T^2*d). The forward does two
+# products (S = QK^T, O = PV); the backward's five counted products are
+# credited four to dK/dV (S, dP, dV, dK) and one to dQ (dQ); the dQ kernel's
+# recomputation of S and dP is executed but not credited.
+KERNELS = {
+    "attn_fwd": ("attn_fwd_bf16.hip", "mfma", 2.0),
+    "attn_bwd_preprocess": ("attn_bwd_bf16.hip", "hbm", 0.0),
+    "attn_bwd_dkdv": ("attn_bwd_bf16.hip", "mfma", 4.0),
+    "attn_bwd_dq": ("attn_bwd_bf16.hip", "mfma", 1.0),
+}
+STAGES = list(KERNELS)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, run a plain 256 MiB device copy (for counter scaling)")
+    return p.parse_args(argv)
+
+
+def source_digest(path: str) -> str:
+    h = hashlib.sha256()
+    for f in sorted({os.path.join(CSRC, "attn_common.h"), path}):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    m_val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not (m_src and m_val):
+        return None
+    if m_src.group(1) != source_digest(os.path.join(CSRC, KERNELS[kernel][0])):
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the float64 oracle (forward + backward) on whole heads of the
+    workload until about target_s seconds have passed."""
+    import numpy as np
+
+    import oracle
+    from causal_flash_attention_amd import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    # inputs of batch row 0 only (the heads timed come from it)
+    qkv, dout = I.attention_inputs(1, w.T, w.n_head, w.head_dim, w.dtype, w.qkv_std, w.dout_std, seed=0)
+    q64, g64 = I.to_float64(qkv, w.dtype), I.to_float64(dout, w.dtype)
+    D = w.head_dim
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        h = done % w.n_head
+        q, k, v = oracle.split_packed_head(q64, 0, h, w.n_head, D)
+        g = g64[0, :, h * D:(h + 1) * D]
+        oracle.head_forward(q, k, v)
+        oracle.head_backward(q, k, v, g)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= w.B * w.n_head:
+            break
+    flops = 7.0 * done * w.T * w.T * D
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.n_head} heads of {w.name} (T={w.T}, d={D}), float64 "
+                  f"forward+backward materialising T x T per head, {el:.1f} s wall, "
+                  f"counted 7*T^2*d FLOPs per head",
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(every (batch, head) is independent, so more GPUs would split the batch or the heads with no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from causal_flash_attention_amd import binding
+    from causal_flash_attention_amd import inputs as I
+    from causal_flash_attention_amd.workloads import BY_NAME, HEADLINE
+
+    w = BY_NAME[args.workload] if args.workload else HEADLINE
+    if w.dtype != "bf16":
+        raise SystemExit("the bench times the bf16 path")
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    C = H * D
+    qkv_h, dout_h = I.attention_inputs(B, T, H, D, w.dtype, w.qkv_std, w.dout_std, seed=0)
+    qkv = torch.from_numpy(qkv_h.view(np.int16)).view(torch.bfloat16).to(dev)
+    dout = torch.from_numpy(dout_h.view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dqkv = torch.empty((B, T, 3 * C), dtype=torch.bfloat16, device=dev)
+    delta = torch.empty(binding.workspace_floats(B, T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.attn_fwd(qkv, out, lse, H, D, stream)
+        binding.attn_bwd(dout, qkv, out, lse, dqkv, delta, H, D, stream)
+
+    def staged_step(evs):
+        evs[0].record(stream)
+        binding.attn_fwd(qkv, out, lse, H, D, stream)
+        evs[1].record(stream)
+        binding.attn_bwd_preprocess(dout, out, lse, delta, H, D, stream)
+        evs[2].record(stream)
+        binding.attn_bwd_dkdv(dout, qkv, delta, dqkv, H, D, stream)
+        evs[3].record(stream)
+        binding.attn_bwd_dq(dout, qkv, delta, dqkv, H, D, stream)
+        evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps.
+    K = args.steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(K):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / K
+
+    # Kernel-timing region: K more steps with events between the kernels.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        staged_step(ev[i])
+    torch.cuda.synchronize()
+    kernel_us = {}
+    for j, name in enumerate(STAGES):
+        kernel_us[name] = 1000.0 * sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+
+    flops = w.counted_flops()
+    tflops = flops["total"] / (ms_per_step * 1e-3) / 1e12
+    unit_flops = float(B) * H * T * T * D  # one causal T x T x d product over all heads
+
+    dom = max(STAGES, key=lambda n: kernel_us[n])
+    _src, bound, units = KERNELS[dom]
+    dur_s = kernel_us[dom] * 1e-6
+    traffic = traffic_from_profile(dom, w.name)
+    if bound == "mfma":
+        achieved = units * unit_flops / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic}
+    else:
+        # preprocess: read dout, out, lse; write the two workspace arrays
+        algo_bytes = 2.0 * B * T * C * 2 + B * H * T * 4 + binding.workspace_floats(B, T, H) * 4
+        achieved = algo_bytes / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    roof["kernel"] = dom
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "n_head": H, "head_dim": D,
+                   "causal": True, "qkv_std": w.qkv_std, "dout_std": w.dout_std,
+                   "counted_gflop_per_step": flops["total"] / 1e9},
+        "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "kernels_us": kernel_us,
+        "host_wall_s": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

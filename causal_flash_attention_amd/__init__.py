@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     backward,
     forward,
     lib,
+    workspace_floats,
 )

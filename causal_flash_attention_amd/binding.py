@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional, Tuple
 
-from .build import LIB_PATH
+from ._paths import LIB_PATH
 
 ATTN_OK = 0
 STATUS_NAMES = {
@@ -35,9 +35,10 @@ _I = ctypes.c_int
 SIGNATURES = {
     "attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
-    "attn_bwd_preprocess": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
-    "attn_bwd_dkdv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
-    "attn_bwd_dq": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_preprocess": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_dkdv": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_dq": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
@@ -141,6 +142,23 @@ def attn_fwd(qkv, out, lse, n_head: int, head_dim: int = 64, stream=None) -> Non
            "attn_fwd" + sfx)
 
 
+def workspace_floats(B: int, T: int, n_head: int) -> int:
+    """Floats the backward workspace must hold: 2 * B * n_head * round_up(T, 64)."""
+    n = int(lib().attn_bwd_workspace_floats(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def _require_ws(delta, B, T, n_head):
+    torch = _torch()
+    if delta is None or not delta.is_cuda or delta.dtype != torch.float32:
+        raise ValueError("delta must be a float32 GPU tensor")
+    if not delta.is_contiguous() or delta.numel() < workspace_floats(B, T, n_head):
+        raise ValueError("delta must be contiguous with at least "
+                         f"{workspace_floats(B, T, n_head)} floats")
+
+
 def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
              stream=None) -> None:
     torch = _torch()
@@ -151,42 +169,41 @@ def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
     _require(out, "out", dt, (B, T, C))
     _require(lse, "lse", torch.float32, (B, n_head, T))
     _require(dqkv, "dqkv", dt, (B, T, 3 * C))
-    _require(delta, "delta", torch.float32, (B, n_head, T))
+    _require_ws(delta, B, T, n_head)
     fn = getattr(lib(), "attn_bwd" + sfx)
     _check(fn(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dqkv), _ptr(delta),
               B, T, n_head, head_dim, _stream_ptr(stream)), "attn_bwd" + sfx)
 
 
-def attn_bwd_preprocess(dout, out, delta, n_head: int, head_dim: int = 64, stream=None) -> None:
+def attn_bwd_preprocess(dout, out, lse, delta, n_head: int, head_dim: int = 64,
+                        stream=None) -> None:
     torch = _torch()
     B, T, C = int(out.shape[0]), int(out.shape[1]), n_head * head_dim
     _require(out, "out", torch.bfloat16, (B, T, C))
     _require(dout, "dout", torch.bfloat16, (B, T, C))
-    _require(delta, "delta", torch.float32, (B, n_head, T))
-    _check(lib().attn_bwd_preprocess(_ptr(dout), _ptr(out), _ptr(delta), B, T, n_head, head_dim,
-                                     _stream_ptr(stream)), "attn_bwd_preprocess")
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require_ws(delta, B, T, n_head)
+    _check(lib().attn_bwd_preprocess(_ptr(dout), _ptr(out), _ptr(lse), _ptr(delta), B, T, n_head,
+                                     head_dim, _stream_ptr(stream)), "attn_bwd_preprocess")
 
 
-def _bwd_stage(name, dout, qkv, lse, delta, dqkv, n_head, head_dim, stream):
+def _bwd_stage(name, dout, qkv, delta, dqkv, n_head, head_dim, stream):
     torch = _torch()
     B, T, C = _dims(qkv, n_head, head_dim)
     _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
     _require(dout, "dout", torch.bfloat16, (B, T, C))
-    _require(lse, "lse", torch.float32, (B, n_head, T))
-    _require(delta, "delta", torch.float32, (B, n_head, T))
     _require(dqkv, "dqkv", torch.bfloat16, (B, T, 3 * C))
-    _check(getattr(lib(), name)(_ptr(dout), _ptr(qkv), _ptr(lse), _ptr(delta), _ptr(dqkv),
+    _require_ws(delta, B, T, n_head)
+    _check(getattr(lib(), name)(_ptr(dout), _ptr(qkv), _ptr(delta), _ptr(dqkv),
                                 B, T, n_head, head_dim, _stream_ptr(stream)), name)
 
 
-def attn_bwd_dkdv(dout, qkv, lse, delta, dqkv, n_head: int, head_dim: int = 64,
-                  stream=None) -> None:
-    _bwd_stage("attn_bwd_dkdv", dout, qkv, lse, delta, dqkv, n_head, head_dim, stream)
+def attn_bwd_dkdv(dout, qkv, delta, dqkv, n_head: int, head_dim: int = 64, stream=None) -> None:
+    _bwd_stage("attn_bwd_dkdv", dout, qkv, delta, dqkv, n_head, head_dim, stream)
 
 
-def attn_bwd_dq(dout, qkv, lse, delta, dqkv, n_head: int, head_dim: int = 64,
-                stream=None) -> None:
-    _bwd_stage("attn_bwd_dq", dout, qkv, lse, delta, dqkv, n_head, head_dim, stream)
+def attn_bwd_dq(dout, qkv, delta, dqkv, n_head: int, head_dim: int = 64, stream=None) -> None:
+    _bwd_stage("attn_bwd_dq", dout, qkv, delta, dqkv, n_head, head_dim, stream)
 
 
 def attn_status_string(status: int) -> str:
@@ -220,6 +237,6 @@ def backward(dout, qkv, out, lse, n_head: int, head_dim: int = 64, stream=None):
     torch = _torch()
     B, T, C = _dims(qkv, n_head, head_dim)
     dqkv = torch.empty_like(qkv)
-    delta = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+    delta = torch.empty(workspace_floats(B, T, n_head), dtype=torch.float32, device=qkv.device)
     attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
     return dqkv

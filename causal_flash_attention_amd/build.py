@@ -10,21 +10,23 @@ import shutil
 import subprocess
 import sys
 
-PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+from causal_flash_attention_amd._paths import LIB_PATH, PKG_DIR
+
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB_NAME = "libcausal_attn.so"
-LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip"]
 
-# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32,
+# -packed-fp32-ops: keep the compiler from forming packed fp32 add/mul/fma,
 # which are avoided on this target; hipcc's host pass warns that it does not
 # know the feature, which is harmless.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results stay in ordinary VGPRs instead of accumulation registers,
+    # which the softmax and rescale would otherwise copy back and forth.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -8,13 +8,15 @@
 
 namespace cattn {
 hipError_t launch_attn_fwd_bf16(const void*, void*, float*, int, int, int, hipStream_t);
-hipError_t launch_attn_bwd_pre_bf16(const void*, const void*, float*, int, int, int, hipStream_t);
-hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, const float*, void*,
-                                     int, int, int, hipStream_t);
-hipError_t launch_attn_bwd_dq_bf16(const void*, const void*, const float*, const float*, void*,
-                                   int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_pre_bf16(const void*, const void*, const float*, float*, int, int, int,
+                                    hipStream_t);
+hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, void*, int, int, int,
+                                     hipStream_t);
+hipError_t launch_attn_bwd_dq_bf16(const void*, const void*, const float*, void*, int, int, int,
+                                   hipStream_t);
 hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
-hipError_t launch_attn_bwd_pre_f32(const float*, const float*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_pre_f32(const float*, const float*, const float*, float*, int, int, int,
+                                   hipStream_t);
 hipError_t launch_attn_bwd_dkdv_f32(const float*, const float*, const float*, const float*, float*,
                                     int, int, int, hipStream_t);
 hipError_t launch_attn_bwd_dq_f32(const float*, const float*, const float*, const float*, float*,
@@ -60,8 +62,10 @@ int check_shape(int B, int T, int H, int d, int elem, bool* empty) {
     if (bt > kMaxBytes / c3 / elem) return fail(ATTN_ERR_TOO_LARGE, "B*T*3*n_head*head_dim overflows");
     const long long blocks = (long long)B * H * ((T + 63) / 64);
     if (blocks > kMaxBlocks) return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
-    // the preprocess grid: 16 rows of (b, t, h) per workgroup in float32
-    if (((long long)B * T * H + 15) / 16 > kMaxBlocks)
+    // the preprocess grid: 16 rows of (b, t, h) per workgroup in float32, plus
+    // one thread per padded workspace row entry
+    const long long tp = ((long long)T + 63) / 64 * 64;
+    if (((long long)B * T * H + 15) / 16 + ((long long)B * H * tp + 255) / 256 > kMaxBlocks)
         return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
     if ((long long)H * d > 0x7fffffffLL / 3) return fail(ATTN_ERR_TOO_LARGE, "3*n_head*head_dim overflows int");
     return ATTN_OK;
@@ -96,12 +100,18 @@ Span span(const void* p, long long bytes, const char* name) {
 }
 
 struct Sizes {
-    long long qkv, bt_c, rows;  // bytes of qkv, bytes of a (B,T,C) tensor, bytes of (B,H,T) fp32
+    // bytes of qkv, of a (B,T,C) tensor, of (B,H,T) fp32, of the backward workspace
+    long long qkv, bt_c, rows, ws;
 };
+
+long long workspace_floats(int B, int T, int H) {
+    const long long tp = ((long long)T + 63) / 64 * 64;
+    return 2LL * B * H * tp;
+}
 
 Sizes sizes(int B, int T, int H, int elem) {
     const long long n = (long long)B * T * H * kHeadDim;
-    return Sizes{3 * n * elem, n * elem, (long long)B * H * T * 4};
+    return Sizes{3 * n * elem, n * elem, (long long)B * H * T * 4, workspace_floats(B, T, H) * 4};
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -130,58 +140,61 @@ int fwd_common(const void* qkv, void* out, float* lse, int B, int T, int H, int 
 
 enum Stage { kPre = 1, kDkdv = 2, kDq = 4, kAll = 7 };
 
+// Backward argument checks and launches. Stage kPre reads dout, out, lse and
+// writes the workspace; kDkdv / kDq read dout, qkv and the workspace (the
+// float32 kernels also lse) and write dqkv.
 int bwd_common(const void* dout, const void* qkv, const void* out, const float* lse, void* dqkv,
-               float* delta, int B, int T, int H, int d, void* stream, int elem, int stages) {
+               float* ws, int B, int T, int H, int d, void* stream, int elem, int stages) {
     g_last_error[0] = '\0';
+    const bool grad = (stages & (kDkdv | kDq)) != 0;
+    const bool need_lse = (stages & kPre) || elem == 4;
     const bool nonempty = !(B == 0 || T == 0 || H == 0);
     if (nonempty) {
         if (!dout) return fail(ATTN_ERR_NULL_PTR, "dout is NULL");
-        if ((stages & (kDkdv | kDq)) && !qkv) return fail(ATTN_ERR_NULL_PTR, "qkv is NULL");
+        if (grad && !qkv) return fail(ATTN_ERR_NULL_PTR, "qkv is NULL");
         if ((stages & kPre) && !out) return fail(ATTN_ERR_NULL_PTR, "out is NULL");
-        if ((stages & (kDkdv | kDq)) && !lse) return fail(ATTN_ERR_NULL_PTR, "lse is NULL");
-        if ((stages & (kDkdv | kDq)) && !dqkv) return fail(ATTN_ERR_NULL_PTR, "dqkv is NULL");
-        if (!delta) return fail(ATTN_ERR_NULL_PTR, "delta is NULL");
+        if (need_lse && !lse) return fail(ATTN_ERR_NULL_PTR, "lse is NULL");
+        if (grad && !dqkv) return fail(ATTN_ERR_NULL_PTR, "dqkv is NULL");
+        if (!ws) return fail(ATTN_ERR_NULL_PTR, "delta (workspace) is NULL");
     }
     bool empty = false;
     int st = check_shape(B, T, H, d, elem, &empty);
     if (st != ATTN_OK || empty) return st;
     if ((st = check_aligned(dout, 16, "dout must be 16-byte aligned")) != ATTN_OK) return st;
-    if ((stages & (kDkdv | kDq)) && (st = check_aligned(qkv, 16, "qkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if (grad && (st = check_aligned(qkv, 16, "qkv must be 16-byte aligned")) != ATTN_OK) return st;
     if ((stages & kPre) && (st = check_aligned(out, 16, "out must be 16-byte aligned")) != ATTN_OK) return st;
-    if ((stages & (kDkdv | kDq)) && (st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
-    if ((stages & (kDkdv | kDq)) && (st = check_aligned(dqkv, 16, "dqkv must be 16-byte aligned")) != ATTN_OK) return st;
-    if ((st = check_aligned(delta, 4, "delta must be 4-byte aligned")) != ATTN_OK) return st;
+    if (need_lse && (st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    if (grad && (st = check_aligned(dqkv, 16, "dqkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(ws, 16, "delta (workspace) must be 16-byte aligned")) != ATTN_OK) return st;
 
     const Sizes z = sizes(B, T, H, elem);
-    Span ins[4];
+    Span ins[5];
     int n_in = 0;
     ins[n_in++] = span(dout, z.bt_c, "dout");
-    if (stages & (kDkdv | kDq)) {
-        ins[n_in++] = span(qkv, z.qkv, "qkv");
-        ins[n_in++] = span(lse, z.rows, "lse");
-    }
+    if (grad) ins[n_in++] = span(qkv, z.qkv, "qkv");
+    if (need_lse) ins[n_in++] = span(lse, z.rows, "lse");
     if (stages & kPre) ins[n_in++] = span(out, z.bt_c, "out");
     Span outs[2];
     int n_out = 0;
-    if (stages & (kDkdv | kDq)) outs[n_out++] = span(dqkv, z.qkv, "dqkv");
-    // delta is written by the preprocess stage and read by the others.
-    if (stages & kPre) outs[n_out++] = span(delta, z.rows, "delta");
-    else ins[n_in++] = span(delta, z.rows, "delta");
+    if (grad) outs[n_out++] = span(dqkv, z.qkv, "dqkv");
+    // The workspace is written by the preprocess stage and read by the others.
+    if (stages & kPre) outs[n_out++] = span(ws, z.ws, "delta");
+    else ins[n_in++] = span(ws, z.ws, "delta");
     if ((st = check_disjoint(outs, n_out, ins, n_in)) != ATTN_OK) return st;
 
     const hipStream_t s = as_stream(stream);
     hipError_t e = hipSuccess;
     if (elem == 2) {
         if (stages & kPre) {
-            e = cattn::launch_attn_bwd_pre_bf16(dout, out, delta, B, T, H, s);
+            e = cattn::launch_attn_bwd_pre_bf16(dout, out, lse, ws, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd preprocess launch");
         }
         if (stages & kDkdv) {
-            e = cattn::launch_attn_bwd_dkdv_bf16(qkv, dout, lse, delta, dqkv, B, T, H, s);
+            e = cattn::launch_attn_bwd_dkdv_bf16(qkv, dout, ws, dqkv, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd dK/dV launch");
         }
         if (stages & kDq) {
-            e = cattn::launch_attn_bwd_dq_bf16(qkv, dout, lse, delta, dqkv, B, T, H, s);
+            e = cattn::launch_attn_bwd_dq_bf16(qkv, dout, ws, dqkv, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd dQ launch");
         }
     } else {
@@ -189,15 +202,16 @@ int bwd_common(const void* dout, const void* qkv, const void* out, const float* 
         const float* f_qkv = static_cast<const float*>(qkv);
         float* f_dqkv = static_cast<float*>(dqkv);
         if (stages & kPre) {
-            e = cattn::launch_attn_bwd_pre_f32(f_dout, static_cast<const float*>(out), delta, B, T, H, s);
+            e = cattn::launch_attn_bwd_pre_f32(f_dout, static_cast<const float*>(out), lse, ws, B,
+                                               T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 preprocess launch");
         }
         if (stages & kDkdv) {
-            e = cattn::launch_attn_bwd_dkdv_f32(f_qkv, f_dout, lse, delta, f_dqkv, B, T, H, s);
+            e = cattn::launch_attn_bwd_dkdv_f32(f_qkv, f_dout, lse, ws, f_dqkv, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 dK/dV launch");
         }
         if (stages & kDq) {
-            e = cattn::launch_attn_bwd_dq_f32(f_qkv, f_dout, lse, delta, f_dqkv, B, T, H, s);
+            e = cattn::launch_attn_bwd_dq_f32(f_qkv, f_dout, lse, ws, f_dqkv, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd_f32 dQ launch");
         }
     }
@@ -218,22 +232,27 @@ int attn_bwd(const void* dout, const void* qkv, const void* out, const float* ls
     return bwd_common(dout, qkv, out, lse, dqkv, delta, B, T, n_head, head_dim, stream, 2, kAll);
 }
 
-int attn_bwd_preprocess(const void* dout, const void* out, float* delta, int B, int T, int n_head,
-                        int head_dim, void* stream) {
-    return bwd_common(dout, nullptr, out, nullptr, nullptr, delta, B, T, n_head, head_dim, stream,
-                      2, kPre);
+int attn_bwd_preprocess(const void* dout, const void* out, const float* lse, float* delta, int B,
+                        int T, int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, nullptr, out, lse, nullptr, delta, B, T, n_head, head_dim, stream, 2,
+                      kPre);
 }
 
-int attn_bwd_dkdv(const void* dout, const void* qkv, const float* lse, const float* delta,
-                  void* dqkv, int B, int T, int n_head, int head_dim, void* stream) {
-    return bwd_common(dout, qkv, nullptr, lse, dqkv, const_cast<float*>(delta), B, T, n_head,
+int attn_bwd_dkdv(const void* dout, const void* qkv, const float* delta, void* dqkv, int B, int T,
+                  int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, nullptr, nullptr, dqkv, const_cast<float*>(delta), B, T, n_head,
                       head_dim, stream, 2, kDkdv);
 }
 
-int attn_bwd_dq(const void* dout, const void* qkv, const float* lse, const float* delta,
-                void* dqkv, int B, int T, int n_head, int head_dim, void* stream) {
-    return bwd_common(dout, qkv, nullptr, lse, dqkv, const_cast<float*>(delta), B, T, n_head,
+int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqkv, int B, int T,
+                int n_head, int head_dim, void* stream) {
+    return bwd_common(dout, qkv, nullptr, nullptr, dqkv, const_cast<float*>(delta), B, T, n_head,
                       head_dim, stream, 2, kDq);
+}
+
+long long attn_bwd_workspace_floats(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    return workspace_floats(B, T, n_head);
 }
 
 int attn_fwd_f32(const float* qkv, float* out, float* lse, int B, int T, int n_head, int head_dim,

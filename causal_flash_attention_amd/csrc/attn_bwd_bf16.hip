@@ -14,73 +14,89 @@
 //
 // The dK/dV and dQ kernels each own disjoint output rows, so the backward
 // uses no atomics and is bitwise reproducible run to run.
+//
+// Workspace (float32, per (batch, head) row padded to Tp = round_up(T, 64)):
+//   ws[0 .. BH*Tp)       D,            0 for t >= T
+//   ws[BH*Tp .. 2*BH*Tp) LSE * log2 e, +inf for t >= T (so P = 0 there)
 #include "attn_common.h"
 
 namespace cattn {
 namespace {
 
+constexpr int ROW_PAD = 64;
+constexpr int NSTAGE = 3;
+
 // ---------------------------------------------------------------------------
-// D[b, h, t] = sum_k dO[b, t, h, k] * O[b, t, h, k]; 8 lanes per (b, t, h).
+// Preprocess. Blocks [0, nb_d): D[b, h, t] = sum_k dO[b,t,h,k] O[b,t,h,k], 8
+// lanes per (b, t, h). Blocks [nb_d, ...): one thread per padded (bh, t):
+// LSE * log2 e, and the padding of both arrays.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
-    const bf16* __restrict__ dout, const bf16* __restrict__ out, float* __restrict__ delta,
-    int T, int H, long long n_rows) {
-    const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int part = threadIdx.x & 7;
-    float acc = 0.0f;
-    if (row < n_rows) {
-        const long long off = row * HEAD_DIM + part * 8;  // rows are (b, t, h) in memory order
-        const bf16x8 g = as_bf16x8(*reinterpret_cast<const u32x4*>(dout + off));
-        const bf16x8 o = as_bf16x8(*reinterpret_cast<const u32x4*>(out + off));
+    const bf16* __restrict__ dout, const bf16* __restrict__ out, const float* __restrict__ lse,
+    float* __restrict__ ws, int T, int Tp, int H, long long n_rows, long long nb_d,
+    long long n_pad_rows) {
+    const long long blk = blockIdx.x;
+    float* __restrict__ dd = ws;
+    float* __restrict__ lse2 = ws + n_pad_rows;
+    if (blk < nb_d) {
+        const long long row = blk * 32 + (threadIdx.x >> 3);
+        const int part = threadIdx.x & 7;
+        float acc = 0.0f;
+        if (row < n_rows) {
+            const long long off = row * HEAD_DIM + part * 8;  // rows are (b, t, h) in memory order
+            const bf16x8 g = as_bf16x8(*reinterpret_cast<const u32x4*>(dout + off));
+            const bf16x8 o = as_bf16x8(*reinterpret_cast<const u32x4*>(out + off));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)g[e], (float)o[e], acc);
-    }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    if (row < n_rows && part == 0) {
-        const long long bt = row / H;
-        const int h = (int)(row - bt * H);
-        const long long b = bt / T;
-        const int t = (int)(bt - b * T);
-        delta[(b * H + h) * T + t] = acc;
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)g[e], (float)o[e], acc);
+        }
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        if (row < n_rows && part == 0) {
+            const long long bt = row / H;
+            const int h = (int)(row - bt * H);
+            const long long b = bt / T;
+            const int t = (int)(bt - b * T);
+            dd[(b * H + h) * Tp + t] = acc;
+        }
+    } else {
+        const long long i = (blk - nb_d) * 256 + threadIdx.x;  // padded (bh, t)
+        if (i < n_pad_rows) {
+            const long long bh = i / Tp;
+            const int t = (int)(i - bh * Tp);
+            if (t < T) {
+                lse2[i] = lse[bh * T + t] * LOG2E;
+            } else {
+                lse2[i] = INFINITY;
+                dd[i] = 0.0f;
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV. One workgroup = 4 waves = 128 keys of one (batch, head); wave w owns
 // keys k0 + 32w .. +31, with K and V of those keys held in registers. Query
-// tiles of 64 rows stream through double-buffered LDS as Q, Q^T, dO, dO^T,
-// LSE*log2(e) and D. Per tile and wave: S = Q K^T and dP = dO V^T on MFMA
-// (lane l%32 owns key l%32), P and dS in registers, then
-// dV^T += dO^T P and dK^T += Q^T dS on MFMA with P and dS fed straight from
-// registers. Query tiles entirely before a wave's keys are skipped.
+// tiles of 64 rows (Q, dO, and their LSE*log2 e and D) stream through a
+// three-stage ring of LDS buffers filled by direct global->LDS loads. Per
+// tile and wave: S = Q K^T and dP = dO V^T on MFMA (lane l%32 owns key l%32),
+// P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS on MFMA with
+// P and dS fed straight from registers and Q^T, dO^T read from the row-major
+// tiles by transposing LDS reads. Query tiles entirely before a wave's keys
+// are skipped.
 // ---------------------------------------------------------------------------
 constexpr int KV_BN = 128;  // keys per workgroup
 constexpr int KV_BM = 64;   // queries per LDS tile
 
-struct DkdvSmem {
-    bf16 q[2][KV_BM * LDS_ROW];
-    bf16 qt[2][HEAD_DIM * LDS_ROW];
-    bf16 g[2][KV_BM * LDS_ROW];
-    bf16 gt[2][HEAD_DIM * LDS_ROW];
-    float lse2[2][KV_BM];
-    float dd[2][KV_BM];
+struct alignas(16) DkdvSmem {
+    bf16 q[NSTAGE][ATILE_ELEMS];
+    bf16 g[NSTAGE][ATILE_ELEMS];
+    float stats[NSTAGE][2 * KV_BM];  // [LSE * log2 e | D] of the tile's queries
 };
 
-__device__ __forceinline__ void stage_rowstats(float* lse2_s, float* dd_s, const float* lse_row,
-                                               const float* d_row, int q0, int T, int tid) {
-    if (tid < KV_BM) {
-        const int q = q0 + tid;
-        lse2_s[tid] = q < T ? lse_row[q] * LOG2E : INFINITY;  // P = 0 past the end
-        dd_s[tid] = q < T ? d_row[q] : 0.0f;
-    }
-}
-
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, bf16* __restrict__ dqkv, int B, int T, int H, int n_kt,
-    float c_log2, float scale) {
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
+    bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_kt, float c_log2, float scale) {
     __shared__ DkdvSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -103,8 +119,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
     const bf16* kbase = qbase + C;
     const bf16* vbase = qbase + 2 * C;
     const bf16* gbase = dout + (long long)b * T * C + h * HEAD_DIM;
-    const float* lse_row = lse + (long long)bh * T;
-    const float* d_row = delta + (long long)bh * T;
+    const float* dd_row = ws + (long long)bh * Tp;
+    const float* lse2_row = ws + (long long)BH * Tp + (long long)bh * Tp;
 
     const int k0 = kt * KV_BN;
     const int kw = k0 + wave * 32;
@@ -123,93 +139,106 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
         }
     }
 
+    // Per-lane LDS offsets: row-major reads of rows qb*32 + l32, chunks 2kk + hf;
+    // transposed reads for d blocks 0 and 1.
+    int roff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) roff[kk] = l32 * 64 + (((2 * kk + hf) ^ swz(l32)) << 3);
+    int troff[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &troff[db][0], &troff[db][1]);
+
     f32x16 dvt[2] = {zero16(), zero16()};  // dV^T, d blocks
     f32x16 dkt[2] = {zero16(), zero16()};  // dK^T / scale, d blocks
 
     const int qt_begin = k0 / KV_BM;
-    const int qt_end = (T + KV_BM - 1) / KV_BM;
+    const int n_it = (T + KV_BM - 1) / KV_BM - qt_begin;
 
-    {
-        const int q0 = qt_begin * KV_BM;
-        TilePair tq = load_tile_pair(qbase, rs, q0, T, tid);
-        TilePair tg = load_tile_pair(gbase, C, q0, T, tid);
-        store_tile_rows(sm.q[0], tq, tid);
-        store_tile_transposed(sm.qt[0], tq, tid);
-        store_tile_rows(sm.g[0], tg, tid);
-        store_tile_transposed(sm.gt[0], tg, tid);
-        stage_rowstats(sm.lse2[0], sm.dd[0], lse_row, d_row, q0, T, tid);
-    }
-    __syncthreads();
+    // Issue the loads of query tile `it` (relative) into stage `st`: Q and dO
+    // by every wave, the row statistics by wave 0 (lanes 0..31, 16 bytes each).
+    auto issue = [&](int it, int st) {
+        const int q0 = (qt_begin + it) * KV_BM;
+        atile_load(sm.q[st], qbase, rs, q0, T, wave, lane);
+        atile_load(sm.g[st], gbase, C, q0, T, wave, lane);
+        if (wave == 0 && lane < 32) {
+            const float* src = (lane < 16 ? lse2_row : dd_row) + q0 + 4 * (lane & 15);
+            __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)sm.stats[st], 16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < NSTAGE - 1; ++j)
+        if (j < n_it) issue(j, j);
 
-    for (int it = qt_begin; it < qt_end; ++it) {
-        const int buf = (it - qt_begin) & 1;
-        const int q0 = it * KV_BM;
-        const bool has_next = it + 1 < qt_end;
-        TilePair nq, ng;
-        if (has_next) {
-            nq = load_tile_pair(qbase, rs, q0 + KV_BM, T, tid);
-            ng = load_tile_pair(gbase, C, q0 + KV_BM, T, tid);
-        }
-        if (q0 + KV_BM - 1 >= kw) {
-            // S = Q K^T and dP = dO V^T : two 32-query blocks each.
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[qb] = zero16();
-                dp[qb] = zero16();
-                const bf16* qp = sm.q[buf] + (qb * 32 + l32) * LDS_ROW + hf * 8;
-                const bf16* gp = sm.g[buf] + (qb * 32 + l32) * LDS_ROW + hf * 8;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    s[qb] = mfma32(lds_read8(qp + kk * 16), kreg[kk], s[qb]);
-                    dp[qb] = mfma32(lds_read8(gp + kk * 16), vreg[kk], dp[qb]);
-                }
-            }
-            // P = exp2(c*s - LSE*log2 e), masked where key > query; dS = P (dP - D).
-            const bool need_mask = q0 < kw + 31;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int qi = qb * 32 + 8 * g4 + 4 * hf;
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][qi]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[buf][qi]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 4 * g4 + r;
-                        float p = fast_exp2(fmaf(s[qb][i], c_log2, -l4[r]));
-                        if (need_mask && my_k > q0 + qi + r) p = 0.0f;
-                        s[qb][i] = p;
-                        dp[qb][i] = p * (dp[qb][i] - d4[r]);
-                    }
-                }
-            bf16x8 pb[4], dsb[4];
-#pragma unroll
-            for (int qc = 0; qc < 4; ++qc) {
-                pb[qc] = c_rows_to_operand(s[qc >> 1], qc & 1);
-                dsb[qc] = c_rows_to_operand(dp[qc >> 1], qc & 1);
-            }
-            // dV^T += dO^T P, dK^T += Q^T dS : K = 64 queries in four chunks.
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const bf16* gtp = sm.gt[buf] + (db * 32 + l32) * LDS_ROW + hf * 8;
-                const bf16* qtp = sm.qt[buf] + (db * 32 + l32) * LDS_ROW + hf * 8;
-#pragma unroll
-                for (int qc = 0; qc < 4; ++qc) {
-                    dvt[db] = mfma32(lds_read8(gtp + qc * 16), pb[qc], dvt[db]);
-                    dkt[db] = mfma32(lds_read8(qtp + qc * 16), dsb[qc], dkt[db]);
-                }
-            }
-        }
-        if (has_next) {
-            const int nb = buf ^ 1;
-            store_tile_rows(sm.q[nb], nq, tid);
-            store_tile_transposed(sm.qt[nb], nq, tid);
-            store_tile_rows(sm.g[nb], ng, tid);
-            store_tile_transposed(sm.gt[nb], ng, tid);
-            stage_rowstats(sm.lse2[nb], sm.dd[nb], lse_row, d_row, q0 + KV_BM, T, tid);
+    for (int it = 0; it < n_it; ++it) {
+        if (it + 1 < n_it) {
+            if (wave == 0) wait_vmem<5>();
+            else wait_vmem<4>();
+        } else {
+            wait_vmem<0>();
         }
         __syncthreads();
+        if (it + NSTAGE - 1 < n_it) issue(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+        const int q0 = (qt_begin + it) * KV_BM;
+        if (q0 + KV_BM - 1 < kw) continue;  // every query of the tile precedes this wave's keys
+        const int st = it % NSTAGE;
+        lds_bf16* qt = atile_view(sm.q[st]);
+        lds_bf16* gt = atile_view(sm.g[st]);
+        typedef __attribute__((address_space(3))) const float lds_f32;
+        typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+        typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+        lds_f32* stats = (lds_f32*)atile_view((const bf16*)sm.stats[st]);
+
+        // S = Q K^T and dP = dO V^T : two 32-query blocks each.
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            s[qb] = zero16();
+            dp[qb] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int o = qb * 32 * 64 + roff[kk];
+                s[qb] = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s[qb]);
+                dp[qb] = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp[qb]);
+            }
+        }
+        // P = exp2(c*s - LSE*log2 e), zero where key > query; dS = P (dP - D).
+        // Only the tile holding this wave's diagonal (q0 == kw rounded down to
+        // 64) has masked entries: query q0 + qi + r < my_k.
+        const bool diag = q0 == (kw & ~(KV_BM - 1));
+        const int lim = my_k - q0 - 4 * hf;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int qi = qb * 32 + 8 * g4 + 4 * hf;
+                const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(stats + qi);
+                const f32x4 d4 = *reinterpret_cast<lds_f32x4*>(stats + KV_BM + qi);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * g4 + r;
+                    float p = fast_exp2(fmaf(s[qb][i], c_log2, -l4[r]));
+                    if (diag && qb * 32 + 8 * g4 + r < lim) p = 0.0f;
+                    s[qb][i] = p;
+                    dp[qb][i] = p * (dp[qb][i] - d4[r]);
+                }
+            }
+        bf16x8 pb[4], dsb[4];
+#pragma unroll
+        for (int qc = 0; qc < 4; ++qc) {
+            pb[qc] = c_rows_to_operand(s[qc >> 1], qc & 1);
+            dsb[qc] = c_rows_to_operand(dp[qc >> 1], qc & 1);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS : K = 64 queries in four chunks.
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            bf16x8 a[4];
+            atile_tr4(gt, troff[db][0], troff[db][1], a);
+#pragma unroll
+            for (int qc = 0; qc < 4; ++qc) dvt[db] = mfma32(a[qc], pb[qc], dvt[db]);
+            atile_tr4(qt, troff[db][0], troff[db][1], a);
+#pragma unroll
+            for (int qc = 0; qc < 4; ++qc) dkt[db] = mfma32(a[qc], dsb[qc], dkt[db]);
+        }
     }
 
     if (my_k < T) {
@@ -232,24 +261,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ. One workgroup = 4 waves = 128 queries of one (batch, head); wave w owns
-// queries q0 + 32w .. +31 with Q, dO, LSE and D of its query in registers.
-// Key tiles of 64 rows stream through double-buffered LDS as K, K^T and V.
-// Per tile and wave: S^T = K Q^T and dP^T = V dO^T on MFMA (lane l%32 owns
-// query l%32), P^T and dS^T in registers, dQ^T += K^T dS^T on MFMA.
+// queries q0 + 32w .. +31 with Q, dO, LSE*log2 e and D of its query in
+// registers. Key tiles of 64 rows (K and V) stream through a three-stage ring
+// of LDS buffers filled by direct global->LDS loads. Per tile and wave:
+// S^T = K Q^T and dP^T = V dO^T on MFMA (lane l%32 owns query l%32), P^T and
+// dS^T in registers, dQ^T += K^T dS^T on MFMA with K^T read from the
+// row-major K tile by transposing LDS reads.
 // ---------------------------------------------------------------------------
 constexpr int DQ_BM = 128;  // queries per workgroup
 constexpr int DQ_BN = 64;   // keys per LDS tile
 
 struct DqSmem {
-    bf16 k[2][DQ_BN * LDS_ROW];
-    bf16 kt[2][HEAD_DIM * LDS_ROW];
-    bf16 v[2][DQ_BN * LDS_ROW];
+    bf16 k[NSTAGE][ATILE_ELEMS];
+    bf16 v[NSTAGE][ATILE_ELEMS];
 };
 
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, bf16* __restrict__ dqkv, int B, int T, int H, int n_qt,
-    float c_log2, float scale) {
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
+    bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_qt, float c_log2, float scale) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -288,75 +317,79 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
             greg[kk] = as_bf16x8(load16(gp + kk * 16, q_ok));
         }
     }
-    const float lse2 = q_ok ? lse[(long long)bh * T + my_q] * LOG2E : INFINITY;
-    const float dd = q_ok ? delta[(long long)bh * T + my_q] : 0.0f;
+    const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
+    const float dd = q_ok ? ws[ws_i] : 0.0f;
+    const float lse2 = q_ok ? ws[(long long)BH * Tp + ws_i] : INFINITY;
+
+    int roff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) roff[kk] = l32 * 64 + (((2 * kk + hf) ^ swz(l32)) << 3);
+    int troff[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &troff[db][0], &troff[db][1]);
 
     f32x16 dqt[2] = {zero16(), zero16()};  // dQ^T / scale, d blocks
 
     const int kend = min(q0 + DQ_BM, T);
     const int n_kt = (kend + DQ_BN - 1) / DQ_BN;
 
-    {
-        TilePair tk = load_tile_pair(kbase, rs, 0, T, tid);
-        TilePair tv = load_tile_pair(vbase, rs, 0, T, tid);
-        store_tile_rows(sm.k[0], tk, tid);
-        store_tile_transposed(sm.kt[0], tk, tid);
-        store_tile_rows(sm.v[0], tv, tid);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NSTAGE - 1; ++j)
+        if (j < n_kt) {
+            atile_load(sm.k[j], kbase, rs, j * DQ_BN, T, wave, lane);
+            atile_load(sm.v[j], vbase, rs, j * DQ_BN, T, wave, lane);
+        }
 
     for (int j = 0; j < n_kt; ++j) {
-        const int buf = j & 1;
-        const int k0 = j * DQ_BN;
-        const bool has_next = j + 1 < n_kt;
-        TilePair nk, nv;
-        if (has_next) {
-            nk = load_tile_pair(kbase, rs, k0 + DQ_BN, T, tid);
-            nv = load_tile_pair(vbase, rs, k0 + DQ_BN, T, tid);
-        }
-        if (k0 <= qw + 31) {
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = zero16();
-                dp[kb] = zero16();
-                const bf16* kp = sm.k[buf] + (kb * 32 + l32) * LDS_ROW + hf * 8;
-                const bf16* vp = sm.v[buf] + (kb * 32 + l32) * LDS_ROW + hf * 8;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    s[kb] = mfma32(lds_read8(kp + kk * 16), qreg[kk], s[kb]);
-                    dp[kb] = mfma32(lds_read8(vp + kk * 16), greg[kk], dp[kb]);
-                }
-            }
-            const bool need_mask = k0 + DQ_BN - 1 > qw;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float p = fast_exp2(fmaf(s[kb][i], c_log2, -lse2));
-                    if (need_mask) {
-                        const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                        if (key > my_q) p = 0.0f;
-                    }
-                    dp[kb][i] = p * (dp[kb][i] - dd);
-                }
-            bf16x8 dsb[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) dsb[kc] = c_rows_to_operand(dp[kc >> 1], kc & 1);
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const bf16* ktp = sm.kt[buf] + (db * 32 + l32) * LDS_ROW + hf * 8;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) dqt[db] = mfma32(lds_read8(ktp + kc * 16), dsb[kc], dqt[db]);
-            }
-        }
-        if (has_next) {
-            const int nb = buf ^ 1;
-            store_tile_rows(sm.k[nb], nk, tid);
-            store_tile_transposed(sm.kt[nb], nk, tid);
-            store_tile_rows(sm.v[nb], nv, tid);
-        }
+        if (j + 1 < n_kt) wait_vmem<4>();
+        else wait_vmem<0>();
         __syncthreads();
+        if (j + NSTAGE - 1 < n_kt) {
+            const int st = (j + NSTAGE - 1) % NSTAGE;
+            atile_load(sm.k[st], kbase, rs, (j + NSTAGE - 1) * DQ_BN, T, wave, lane);
+            atile_load(sm.v[st], vbase, rs, (j + NSTAGE - 1) * DQ_BN, T, wave, lane);
+        }
+        const int k0 = j * DQ_BN;
+        if (k0 > qw + 31) continue;  // whole tile after this wave's queries
+        const int st = j % NSTAGE;
+        lds_bf16* kt = atile_view(sm.k[st]);
+        lds_bf16* vt = atile_view(sm.v[st]);
+        typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = zero16();
+            dp[kb] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int o = kb * 32 * 64 + roff[kk];
+                s[kb] = mfma32(*reinterpret_cast<lds_bf16x8*>(kt + o), qreg[kk], s[kb]);
+                dp[kb] = mfma32(*reinterpret_cast<lds_bf16x8*>(vt + o), greg[kk], dp[kb]);
+            }
+        }
+        // Only the tile holding this wave's diagonal (k0 == qw rounded down
+        // to 64) has masked entries: key k0 + kb*32 + 8(i/4) + 4hf + (i%4) > my_q.
+        const bool diag = k0 == (qw & ~(DQ_BN - 1));
+        const int lim = my_q - k0 - 4 * hf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float p = fast_exp2(fmaf(s[kb][i], c_log2, -lse2));
+                if (diag && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.0f;
+                dp[kb][i] = p * (dp[kb][i] - dd);
+            }
+        bf16x8 dsb[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) dsb[kc] = c_rows_to_operand(dp[kc >> 1], kc & 1);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            bf16x8 a[4];
+            atile_tr4(kt, troff[db][0], troff[db][1], a);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) dqt[db] = mfma32(a[kc], dsb[kc], dqt[db]);
+        }
     }
 
     if (q_ok) {
@@ -376,35 +409,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_attn_bwd_pre_bf16(const void* dout, const void* out, float* delta, int B, int T,
-                                    int H, hipStream_t stream) {
+int bwd_padded_rows(int T) { return (T + ROW_PAD - 1) / ROW_PAD * ROW_PAD; }
+
+hipError_t launch_attn_bwd_pre_bf16(const void* dout, const void* out, const float* lse, float* ws,
+                                    int B, int T, int H, hipStream_t stream) {
+    const int Tp = bwd_padded_rows(T);
     const long long n_rows = (long long)B * T * H;
-    const long long blocks = (n_rows + 31) / 32;
-    hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const bf16*>(dout), static_cast<const bf16*>(out), delta, T, H,
-                       n_rows);
+    const long long nb_d = (n_rows + 31) / 32;
+    const long long n_pad_rows = (long long)B * H * Tp;
+    const long long nb_l = (n_pad_rows + 255) / 256;
+    hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)(nb_d + nb_l)), dim3(256), 0,
+                       stream, static_cast<const bf16*>(dout), static_cast<const bf16*>(out), lse,
+                       ws, T, Tp, H, n_rows, nb_d, n_pad_rows);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dkdv_bf16(const void* qkv, const void* dout, const float* lse,
-                                     const float* delta, void* dqkv, int B, int T, int H,
-                                     hipStream_t stream) {
+hipError_t launch_attn_bwd_dkdv_bf16(const void* qkv, const void* dout, const float* ws, void* dqkv,
+                                     int B, int T, int H, hipStream_t stream) {
     const int n_kt = (T + KV_BN - 1) / KV_BN;
     const long long blocks = (long long)B * H * n_kt;
     hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), lse, delta,
-                       static_cast<bf16*>(dqkv), B, T, H, n_kt, LOG2E / 8.0f, 0.125f);
+                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), ws,
+                       static_cast<bf16*>(dqkv), B, T, bwd_padded_rows(T), H, n_kt,
+                       LOG2E / 8.0f, 0.125f);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dq_bf16(const void* qkv, const void* dout, const float* lse,
-                                   const float* delta, void* dqkv, int B, int T, int H,
-                                   hipStream_t stream) {
+hipError_t launch_attn_bwd_dq_bf16(const void* qkv, const void* dout, const float* ws, void* dqkv,
+                                   int B, int T, int H, hipStream_t stream) {
     const int n_qt = (T + DQ_BM - 1) / DQ_BM;
     const long long blocks = (long long)B * H * n_qt;
     hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), lse, delta,
-                       static_cast<bf16*>(dqkv), B, T, H, n_qt, LOG2E / 8.0f, 0.125f);
+                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), ws,
+                       static_cast<bf16*>(dqkv), B, T, bwd_padded_rows(T), H, n_qt,
+                       LOG2E / 8.0f, 0.125f);
     return hipGetLastError();
 }
 

@@ -98,43 +98,159 @@ __device__ __forceinline__ int perm16(int k) {
     return (k & ~15) | (pg << 2) | (k & 3);
 }
 
-// Stage one 64 x 64 bf16 tile of rows [r0, r0+64) of a strided matrix into
-// LDS. Thread t (of 256) owns rows 2*(t/8) and 2*(t/8)+1, columns 8*(t%8)..+7.
-// Rows at or beyond `nrows` read as zero.
+// Staging of 64 x 64 bf16 tiles (rows [r0, r0 + 64) of a strided matrix)
+// through registers into LDS. Thread t (of 256) owns rows 2*(t%32) and
+// 2*(t%32)+1, column chunk t/32 (8 bf16). With this ownership the transposed
+// copy below is free of LDS bank conflicts: the 64 lanes of a wave write 64
+// distinct banks for every element.
 struct TilePair {
     u32x4 a;  // row 2p
     u32x4 b;  // row 2p + 1
 };
 
+__device__ __forceinline__ int tile_rp(int tid) { return tid & 31; }
+__device__ __forceinline__ int tile_cc(int tid) { return tid >> 5; }
+
+// Rows at or beyond `nrows` read as zero; `full` (uniform) promises that all
+// 64 rows exist and skips the checks.
 __device__ __forceinline__ TilePair load_tile_pair(const bf16* base, long long row_stride,
-                                                   int r0, int nrows, int tid) {
-    const int rp = tid >> 3, cc = tid & 7;
-    const int ra = r0 + 2 * rp, rb = ra + 1;
+                                                   int r0, int nrows, int tid, bool full) {
+    const int ra = r0 + 2 * tile_rp(tid), rb = ra + 1;
+    const bf16* pa = base + (long long)ra * row_stride + tile_cc(tid) * 8;
     TilePair t;
-    t.a = load16(base + (long long)ra * row_stride + cc * 8, ra < nrows);
-    t.b = load16(base + (long long)rb * row_stride + cc * 8, rb < nrows);
+    if (full) {
+        t.a = *reinterpret_cast<const u32x4*>(pa);
+        t.b = *reinterpret_cast<const u32x4*>(pa + row_stride);
+    } else {
+        t.a = load16(pa, ra < nrows);
+        t.b = load16(pa + row_stride, rb < nrows);
+    }
     return t;
 }
 
 // Row-major copy: lds[row][col], padded rows.
 __device__ __forceinline__ void store_tile_rows(bf16* lds, const TilePair& t, int tid) {
-    const int rp = tid >> 3, cc = tid & 7;
-    lds_write16(lds + (2 * rp) * LDS_ROW + cc * 8, t.a);
-    lds_write16(lds + (2 * rp + 1) * LDS_ROW + cc * 8, t.b);
+    const int r = 2 * tile_rp(tid), c = tile_cc(tid) * 8;
+    lds_write16(lds + r * LDS_ROW + c, t.a);
+    lds_write16(lds + (r + 1) * LDS_ROW + c, t.b);
 }
 
 // Transposed copy: lds[col][perm16(row)], padded rows. Rows 2p and 2p+1 stay
 // adjacent under perm16, so each column pair is one 32-bit LDS write.
 __device__ __forceinline__ void store_tile_transposed(bf16* lds, const TilePair& t, int tid) {
-    const int rp = tid >> 3, cc = tid & 7;
-    const int pos = perm16(2 * rp);
+    const int pos = perm16(2 * tile_rp(tid));
+    bf16* col0 = lds + tile_cc(tid) * 8 * LDS_ROW + pos;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const unsigned int wa = t.a[e >> 1], wb = t.b[e >> 1];
-        const unsigned int lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-        const unsigned int hi = (e & 1) ? (wb >> 16) : (wb & 0xffffu);
-        *reinterpret_cast<unsigned int*>(lds + (cc * 8 + e) * LDS_ROW + pos) = lo | (hi << 16);
+    for (int w = 0; w < 4; ++w) {
+        // bytes {a.lo, b.lo} and {a.hi, b.hi} of word w: columns 2w and 2w+1
+        const unsigned int even = __builtin_amdgcn_perm(t.b[w], t.a[w], 0x05040100u);
+        const unsigned int odd = __builtin_amdgcn_perm(t.b[w], t.a[w], 0x07060302u);
+        *reinterpret_cast<unsigned int*>(col0 + (2 * w) * LDS_ROW) = even;
+        *reinterpret_cast<unsigned int*>(col0 + (2 * w + 1) * LDS_ROW) = odd;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Asynchronous tiles: 64 rows x 64 bf16, 128-byte rows with no padding,
+// filled by direct global->LDS loads (no VGPRs, no LDS write instructions)
+// and read either row-major (ds_read_b128) or transposed (ds_read_b64_tr_b16).
+// The 16-byte chunk c of row r sits at chunk c ^ swz(r); swz maps r/2 to a
+// permutation of 0..7 whose consecutive pairs differ in bit 2, which keeps
+// both read patterns free of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int ATILE_ELEMS = 64 * 64;
+
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Issue the loads of rows [r0, r0 + 64) of a strided bf16 matrix into an LDS
+// tile; rows past `nrows` repeat row nrows - 1 (callers mask them). Wave w
+// (of 4) loads tile rows 16w .. 16w + 15: two instructions, each writing 8
+// whole rows (1 KB) at lane-contiguous LDS addresses.
+__device__ __forceinline__ void atile_load(bf16* tile, const bf16* base, long long row_stride,
+                                           int r0, int nrows, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = 16 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ swz(tr);
+        const int row = min(r0 + tr, nrows - 1);
+        const bf16* g = base + (long long)row * row_stride + c * 8;
+        __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(tile + (16 * wave + 8 * i) * 64), 16, 0, 0);
+    }
+}
+
+// LDS address of a tile as seen by its readers. The direct loads above write
+// a whole wave's 1 KB per instruction, but the compiler models them as
+// writing only the 16 bytes at the base it is given, and would otherwise fold
+// reads of the rest of the tile to undefined values. Passing the address
+// through an empty asm statement (after the barrier that publishes the tile)
+// hides where it points.
+typedef __attribute__((address_space(3))) const bf16 lds_bf16;
+
+__device__ __forceinline__ lds_bf16* atile_view(const bf16* tile) {
+    unsigned int a = (unsigned int)(uintptr_t)(lds_bf16*)tile;
+    asm volatile("" : "+v"(a));
+    return (lds_bf16*)(uintptr_t)a;
+}
+
+// Row-major operand: 8 bf16 of tile row r, logical 16-byte chunk c.
+__device__ __forceinline__ bf16x8 atile_row(lds_bf16* tile, int r, int c) {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    return *reinterpret_cast<lds_bf16x8*>(tile + r * 64 + ((c ^ swz(r)) << 3));
+}
+
+
+// Offsets (in bf16 elements) of the two transposed reads that build the
+// A operand X^T (rows d = 32*db + l%32, k = tile rows 16*kc + {4h..4h+3,
+// 8+4h..8+4h+3}) for kc = 0; add 16*64*kc for other chunks (swz is periodic
+// in 16 rows). ds_read_b64_tr_b16 hands lane i of each 16-lane group element
+// (i % 4) of the 8-byte pieces addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4 of that group, so lane i addresses row 4h + i/4 at columns
+// 32*db + 16*((l/16)%2) + 4*(i%4).
+__device__ __forceinline__ void atile_tr_offsets(int lane, int db, int* off0, int* off1) {
+    const int i = lane & 15, grp = lane >> 4, h = grp >> 1;
+    const int d = db * 32 + 16 * (grp & 1) + 4 * (i & 3);
+    const int r0 = 4 * h + (i >> 2), r1 = r0 + 8;
+    *off0 = r0 * 64 + (((d >> 3) ^ swz(r0)) << 3) + (d & 7);
+    *off1 = r1 * 64 + (((d >> 3) ^ swz(r1)) << 3) + (d & 7);
+}
+
+// The four A operands X^T of one d block (kc = 0..3) in one go: eight
+// transposing reads and a wait for them inside the same asm statement, so no
+// read is left in flight when the statement ends. (Through the compiler
+// intrinsic, each such read would make the compiler wait for every pending
+// direct global->LDS load first, which would drain the prefetch pipeline.)
+__device__ __forceinline__ void atile_tr4(lds_bf16* tile, int off0, int off1, bf16x8 out[4]) {
+    const unsigned int a0 = (unsigned int)(uintptr_t)(tile + off0);
+    const unsigned int a1 = (unsigned int)(uintptr_t)(tile + off1);
+    u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(a0), "v"(a1));
+    const u32x2 lo[4] = {r0, r2, r4, r6}, hi[4] = {r1, r3, r5, r7};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 v = {lo[kc][0], lo[kc][1], hi[kc][0], hi[kc][1]};
+        out[kc] = as_bf16x8(v);
+    }
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Value of the other lane half (lane ^ 32).

@@ -90,31 +90,53 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(const float* __restri
     }
 }
 
+// Workspace layout shared with the bf16 path: per (batch, head) row padded to
+// Tp = round_up(T, 64), D in ws[0 .. BH*Tp) and LSE * log2 e in the second
+// half (0 and +inf past T). Blocks [0, nb_d) compute D, 16 lanes per row;
+// the rest fill the second half and the padding, one thread per entry.
 __global__ __launch_bounds__(256) void attn_bwd_pre_f32_kernel(const float* __restrict__ dout,
                                                                const float* __restrict__ out,
-                                                               float* __restrict__ delta, int T,
-                                                               int H, long long n_rows) {
-    const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;
-    float acc = 0.f;
-    if (row < n_rows) {
-        const f32x4 g = *reinterpret_cast<const f32x4*>(dout + row * HEAD_DIM + 4 * part);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(out + row * HEAD_DIM + 4 * part);
-        acc = g[0] * o[0];
-        acc = fmaf(g[1], o[1], acc);
-        acc = fmaf(g[2], o[2], acc);
-        acc = fmaf(g[3], o[3], acc);
-    }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc += __shfl_xor(acc, 8, 64);
-    if (row < n_rows && part == 0) {
-        const long long bt = row / H;
-        const int h = (int)(row - bt * H);
-        const long long b = bt / T;
-        const int t = (int)(bt - b * T);
-        delta[(b * H + h) * T + t] = acc;
+                                                               const float* __restrict__ lse,
+                                                               float* __restrict__ ws, int T,
+                                                               int Tp, int H, long long n_rows,
+                                                               long long nb_d,
+                                                               long long n_pad_rows) {
+    const long long blk = blockIdx.x;
+    if (blk < nb_d) {
+        const long long row = blk * 16 + (threadIdx.x >> 4);
+        const int part = threadIdx.x & 15;
+        float acc = 0.f;
+        if (row < n_rows) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(dout + row * HEAD_DIM + 4 * part);
+            const f32x4 o = *reinterpret_cast<const f32x4*>(out + row * HEAD_DIM + 4 * part);
+            acc = g[0] * o[0];
+            acc = fmaf(g[1], o[1], acc);
+            acc = fmaf(g[2], o[2], acc);
+            acc = fmaf(g[3], o[3], acc);
+        }
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        acc += __shfl_xor(acc, 8, 64);
+        if (row < n_rows && part == 0) {
+            const long long bt = row / H;
+            const int h = (int)(row - bt * H);
+            const long long b = bt / T;
+            const int t = (int)(bt - b * T);
+            ws[(b * H + h) * Tp + t] = acc;
+        }
+    } else {
+        const long long i = (blk - nb_d) * 256 + threadIdx.x;
+        if (i < n_pad_rows) {
+            const long long bh = i / Tp;
+            const int t = (int)(i - bh * Tp);
+            if (t < T) {
+                ws[n_pad_rows + i] = lse[bh * T + t] * LOG2E;
+            } else {
+                ws[n_pad_rows + i] = INFINITY;
+                ws[i] = 0.f;
+            }
+        }
     }
 }
 
@@ -122,7 +144,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_f32_kernel(const float* __re
 // these keys to the end of the sequence.
 __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
     const float* __restrict__ qkv, const float* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dqkv, int B, int T, int H, int n_rt,
+    const float* __restrict__ ws, float* __restrict__ dqkv, int B, int T, int Tp, int H, int n_rt,
     float scale) {
     __shared__ F32Tiles sm;
     const int tid = threadIdx.x, row = tid & 63, half = tid >> 6;
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
     const float* qbase = qkv + (long long)b * T * rs + h * HEAD_DIM;
     const float* gbase = dout + (long long)b * T * C + h * HEAD_DIM;
     const float* lse_row = lse + (long long)bh * T;
-    const float* d_row = delta + (long long)bh * T;
+    const float* d_row = ws + (long long)bh * Tp;
     const int k = rt * F_ROWS + row;
     const bool ok = k < T;
 
@@ -185,7 +207,7 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
 // dQ for 64 queries; streams key tiles up to the diagonal.
 __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(
     const float* __restrict__ qkv, const float* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dqkv, int B, int T, int H, int n_rt,
+    const float* __restrict__ ws, float* __restrict__ dqkv, int B, int T, int Tp, int H, int n_rt,
     float scale) {
     __shared__ F32Tiles sm;
     const int tid = threadIdx.x, row = tid & 63, half = tid >> 6;
@@ -205,7 +227,7 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(
         gv[c] = ok ? gbase[(long long)q * C + c] : 0.f;
     }
     const float lq = ok ? lse[(long long)bh * T + q] : 0.f;
-    const float dq_d = ok ? delta[(long long)bh * T + q] : 0.f;
+    const float dq_d = ok ? ws[(long long)bh * Tp + q] : 0.f;
     float dq[HEAD_DIM / 2];
 #pragma unroll
     for (int c = 0; c < HEAD_DIM / 2; ++c) dq[c] = 0.f;
@@ -245,32 +267,37 @@ hipError_t launch_attn_fwd_f32(const float* qkv, float* out, float* lse, int B, 
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_pre_f32(const float* dout, const float* out, float* delta, int B,
-                                   int T, int H, hipStream_t stream) {
+int bwd_padded_rows(int T);
+
+hipError_t launch_attn_bwd_pre_f32(const float* dout, const float* out, const float* lse,
+                                   float* ws, int B, int T, int H, hipStream_t stream) {
+    const int Tp = bwd_padded_rows(T);
     const long long n_rows = (long long)B * T * H;
-    const long long blocks = (n_rows + 15) / 16;
-    hipLaunchKernelGGL(attn_bwd_pre_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dout,
-                       out, delta, T, H, n_rows);
+    const long long nb_d = (n_rows + 15) / 16;
+    const long long n_pad_rows = (long long)B * H * Tp;
+    const long long nb_l = (n_pad_rows + 255) / 256;
+    hipLaunchKernelGGL(attn_bwd_pre_f32_kernel, dim3((unsigned)(nb_d + nb_l)), dim3(256), 0,
+                       stream, dout, out, lse, ws, T, Tp, H, n_rows, nb_d, n_pad_rows);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkdv_f32(const float* qkv, const float* dout, const float* lse,
-                                    const float* delta, float* dqkv, int B, int T, int H,
+                                    const float* ws, float* dqkv, int B, int T, int H,
                                     hipStream_t stream) {
     const int n_rt = (T + F_ROWS - 1) / F_ROWS;
     const long long blocks = (long long)B * H * n_rt;
     hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)blocks), dim3(128), 0, stream, qkv,
-                       dout, lse, delta, dqkv, B, T, H, n_rt, 0.125f);
+                       dout, lse, ws, dqkv, B, T, bwd_padded_rows(T), H, n_rt, 0.125f);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dq_f32(const float* qkv, const float* dout, const float* lse,
-                                  const float* delta, float* dqkv, int B, int T, int H,
+                                  const float* ws, float* dqkv, int B, int T, int H,
                                   hipStream_t stream) {
     const int n_rt = (T + F_ROWS - 1) / F_ROWS;
     const long long blocks = (long long)B * H * n_rt;
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)blocks), dim3(128), 0, stream, qkv,
-                       dout, lse, delta, dqkv, B, T, H, n_rt, 0.125f);
+                       dout, lse, ws, dqkv, B, T, bwd_padded_rows(T), H, n_rt, 0.125f);
     return hipGetLastError();
 }
 

@@ -6,25 +6,40 @@
 // the theprofessional.online summary, row "flash attention"), written for
 // CDNA4 from the definition rather than from any published kernel.
 //
-// One workgroup = 4 waves = 128 queries of one (batch, head); wave w owns
-// queries q0 + 32w .. q0 + 32w + 31. Key/value tiles of 64 rows stream
-// through double-buffered LDS (K row-major, V transposed). Per tile, each
-// wave computes S^T = K Q^T on MFMA (so that lane l%32 owns query l%32 and
-// the row statistics are per lane), applies the causal mask only on tiles
-// that straddle its diagonal, updates the running max / sum in base 2, and
-// accumulates O^T += V^T P^T on MFMA with P^T fed straight from registers.
-// Tiles entirely above a wave's diagonal are skipped.
+// One workgroup = 4 waves = 4 * 32 * QB queries of one (batch, head); wave w
+// owns QB blocks of 32 queries. Key/value tiles of 64 rows stream through a
+// three-stage ring of LDS buffers filled by direct global->LDS loads, so two
+// tiles are in flight while a third is consumed. Per tile, a wave computes
+// S^T = K Q^T on MFMA (lane l%32 owns query l%32, so row statistics live in
+// one lane pair), masks only the tile on its diagonal, and accumulates
+// O^T += V^T P^T on MFMA with P^T fed straight from registers and V^T read
+// from the row-major V tile by transposing LDS reads. Each LDS operand read
+// feeds all QB query blocks. Tiles above a wave's diagonal are skipped.
+//
+// Softmax in base 2 with a lazily updated running max: the accumulator is
+// rescaled only when some row's tile max exceeds its running max by more
+// than 2^8; otherwise the stale max is kept and P may reach 2^8, which fp32
+// and bf16 hold exactly as well as values below 1. The result is the same
+// function: O = acc / l and LSE = ln 2 * (m + log2 l) for whichever m was used.
 #include "attn_common.h"
+
+#ifndef CATTN_FWD_QB
+#define CATTN_FWD_QB 2
+#endif
 
 namespace cattn {
 namespace {
 
-constexpr int FWD_BM = 128;  // queries per workgroup
-constexpr int FWD_BN = 64;   // keys per LDS tile
+constexpr int FWD_QB = CATTN_FWD_QB;  // 32-query blocks per wave
+constexpr int FWD_BM = 128 * FWD_QB;  // queries per workgroup
+constexpr int FWD_BN = 64;            // keys per tile
+constexpr int NSTAGE = 3;
+constexpr int LOADS_PER_TILE = 4;     // per wave: 2 for K, 2 for V
+constexpr float RESCALE_LOG2 = 8.0f;
 
 struct FwdSmem {
-    bf16 k[2][FWD_BN * LDS_ROW];     // K tile, row-major [key][d]
-    bf16 vt[2][HEAD_DIM * LDS_ROW];  // V tile, transposed [d][perm16(key)]
+    bf16 k[NSTAGE][ATILE_ELEMS];  // K tiles, row-major [key][d] (swizzled)
+    bf16 v[NSTAGE][ATILE_ELEMS];  // V tiles, row-major [key][d] (swizzled)
 };
 
 __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
@@ -56,118 +71,162 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
     const bf16* vbase = qbase + 2 * C;
 
     const int q0 = qt * FWD_BM;
-    const int qw = q0 + wave * 32;
-    const int my_q = qw + l32;
+    const int qw = q0 + wave * 32 * FWD_QB;  // first query of this wave
 
-    // Q^T operand (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of query my_q.
-    bf16x8 qreg[4];
-    {
-        const bool ok = my_q < T;
-        const bf16* p = qbase + (long long)my_q * rs + hf * 8;
+    // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of each block's query.
+    bf16x8 qreg[FWD_QB][4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qreg[kk] = as_bf16x8(load16(p + kk * 16, ok));
+    for (int qb = 0; qb < FWD_QB; ++qb) {
+        const int q = qw + 32 * qb + l32;
+        const bf16* p = qbase + (long long)q * rs + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qreg[qb][kk] = as_bf16x8(load16(p + kk * 16, q < T));
     }
 
     const int kend = min(q0 + FWD_BM, T);
     const int n_kt = (kend + FWD_BN - 1) / FWD_BN;
 
-    float m_run = -INFINITY;  // running max of scale*log2(e)*s
-    float l_run = 0.0f;       // this lane half's share of the running sum
-    f32x16 acc[2] = {zero16(), zero16()};  // O^T, d blocks 0..31 and 32..63
+    // Per-lane LDS offsets: K rows kb*32 + l32 at chunks 2kk + hf; V^T reads.
+    int koff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = l32 * 64 + (((2 * kk + hf) ^ swz(l32)) << 3);
+    int voff[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &voff[db][0], &voff[db][1]);
 
-    {
-        TilePair kt = load_tile_pair(kbase, rs, 0, T, tid);
-        TilePair vt = load_tile_pair(vbase, rs, 0, T, tid);
-        store_tile_rows(sm.k[0], kt, tid);
-        store_tile_transposed(sm.vt[0], vt, tid);
+    float m_run[FWD_QB], l_run[FWD_QB];
+    f32x16 acc[FWD_QB][2];  // O^T per (query block, d block)
+#pragma unroll
+    for (int qb = 0; qb < FWD_QB; ++qb) {
+        m_run[qb] = -INFINITY;  // running max of c*s
+        l_run[qb] = 0.0f;       // this lane half's share of the row sum
+        acc[qb][0] = acc[qb][1] = zero16();
     }
-    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < NSTAGE - 1; ++j)
+        if (j < n_kt) {
+            atile_load(sm.k[j], kbase, rs, j * FWD_BN, T, wave, lane);
+            atile_load(sm.v[j], vbase, rs, j * FWD_BN, T, wave, lane);
+        }
 
     for (int j = 0; j < n_kt; ++j) {
-        const int buf = j & 1;
-        const int k0 = j * FWD_BN;
-        const bool has_next = j + 1 < n_kt;
-        TilePair nk, nv;
-        if (has_next) {
-            nk = load_tile_pair(kbase, rs, k0 + FWD_BN, T, tid);
-            nv = load_tile_pair(vbase, rs, k0 + FWD_BN, T, tid);
+        // Tile j has landed once at most the next tile's loads are pending.
+        if (j + 1 < n_kt) wait_vmem<LOADS_PER_TILE>();
+        else wait_vmem<0>();
+        __syncthreads();
+        if (j + NSTAGE - 1 < n_kt) {
+            const int st = (j + NSTAGE - 1) % NSTAGE;
+            atile_load(sm.k[st], kbase, rs, (j + NSTAGE - 1) * FWD_BN, T, wave, lane);
+            atile_load(sm.v[st], vbase, rs, (j + NSTAGE - 1) * FWD_BN, T, wave, lane);
         }
-        if (k0 <= qw + 31) {
-            // S^T = K Q^T : two 32-key blocks.
-            f32x16 s[2];
+        const int k0 = j * FWD_BN;
+        if (k0 > qw + 32 * FWD_QB - 1) continue;  // whole tile above this wave's diagonal
+        const int st = j % NSTAGE;
+        lds_bf16* kt = atile_view(sm.k[st]);
+        lds_bf16* vt = atile_view(sm.v[st]);
+
+        // S^T = K Q^T for every query block; each K operand read feeds QB MFMAs.
+        f32x16 s[FWD_QB][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = zero16();
-                const bf16* kp = sm.k[buf] + (kb * 32 + l32) * LDS_ROW + hf * 8;
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) s[kb] = mfma32(lds_read8(kp + kk * 16), qreg[kk], s[kb]);
+            for (int qb = 0; qb < FWD_QB; ++qb) s[qb][kb] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+                const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(kt + kb * 32 * 64 + koff[kk]);
+#pragma unroll
+                for (int qb = 0; qb < FWD_QB; ++qb) s[qb][kb] = mfma32(a, qreg[qb][kk], s[qb][kb]);
             }
-            if (k0 + FWD_BN - 1 > qw) {
+        }
+        // Causal mask on the tile that holds a block's diagonal: key > query -> -inf.
+#pragma unroll
+        for (int qb = 0; qb < FWD_QB; ++qb) {
+            const int qblk = qw + 32 * qb;
+            if (k0 + FWD_BN - 1 > qblk) {
+                const int lim = qblk - k0 + l32 - 4 * hf;  // key - k0 must be <= this
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                        if (key > my_q) s[kb][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[qb][kb][i] = -INFINITY;
             }
-            float mx = s[0][0];
+        }
+        float mt[FWD_QB];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < FWD_QB; ++qb) {
+            float mx = s[qb][0][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
             mx = fmaxf(mx, swap_halves(mx));
-            const float m_new = fmaxf(m_run, mx * c_log2);
-            const float alpha = fast_exp2(m_run - m_new);
+            mt[qb] = mx * c_log2;
+            grow |= mt[qb] > m_run[qb] + RESCALE_LOG2;
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int qb = 0; qb < FWD_QB; ++qb) {
+                const float m_new = fmaxf(m_run[qb], mt[qb]);
+                const float alpha = fast_exp2(m_run[qb] - m_new);
+                l_run[qb] *= alpha;
+                m_run[qb] = m_new;
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
+            }
+        }
+        bf16x8 pb[FWD_QB][4];
+#pragma unroll
+        for (int qb = 0; qb < FWD_QB; ++qb) {
             float rsum = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(fmaf(s[kb][i], c_log2, -m_new));
-                    s[kb][i] = p;
+                    const float p = fast_exp2(fmaf(s[qb][kb][i], c_log2, -m_run[qb]));
+                    s[qb][kb][i] = p;
                     rsum += p;
                 }
-            l_run = fmaf(l_run, alpha, rsum);
-            m_run = m_new;
+            l_run[qb] += rsum;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) pb[qb][kc] = c_rows_to_operand(s[qb][kc >> 1], kc & 1);
+        }
+        // O^T += V^T P^T over four 16-key chunks; each V^T operand feeds QB MFMAs.
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            bf16x8 a[4];
+            atile_tr4(vt, voff[db][0], voff[db][1], a);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+                for (int qb = 0; qb < FWD_QB; ++qb) acc[qb][db] = mfma32(a[kc], pb[qb][kc], acc[qb][db]);
+        }
+    }
+
+    // Epilogue: O = acc / l (rounded to bf16), LSE = ln 2 * (m + log2 l).
+#pragma unroll
+    for (int qb = 0; qb < FWD_QB; ++qb) {
+        const int q = qw + 32 * qb + l32;
+        const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+        const float inv = 1.0f / l_tot;
+        if (q < T) {
+            bf16* op = out + ((long long)b * T + q) * C + h * HEAD_DIM;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-
-            // O^T += V^T P^T over four 16-key chunks.
-            bf16x8 pb[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) pb[kc] = c_rows_to_operand(s[kc >> 1], kc & 1);
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const bf16* vp = sm.vt[buf] + (db * 32 + l32) * LDS_ROW + hf * 8;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) acc[db] = mfma32(lds_read8(vp + kc * 16), pb[kc], acc[db]);
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + 8 * g + 4 * hf;
+                    const f32x16& a = acc[qb][db];
+                    *reinterpret_cast<u32x2*>(op + d) =
+                        to_bf16x4_bits(a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv,
+                                       a[4 * g + 3] * inv);
+                }
+            if (hf == 0) lse[(long long)bh * T + q] = (m_run[qb] + log2f(l_tot)) * LN2;
         }
-        if (has_next) {
-            store_tile_rows(sm.k[buf ^ 1], nk, tid);
-            store_tile_transposed(sm.vt[buf ^ 1], nv, tid);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue: O = acc / l (rounded to bf16), LSE = ln(sum) + max in natural units.
-    const float l_tot = l_run + swap_halves(l_run);
-    const float inv = 1.0f / l_tot;
-    if (my_q < T) {
-        bf16* op = out + ((long long)b * T + my_q) * C + h * HEAD_DIM;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + 8 * g + 4 * hf;
-                *reinterpret_cast<u32x2*>(op + d) =
-                    to_bf16x4_bits(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                                   acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-            }
-        if (hf == 0) lse[(long long)bh * T + my_q] = (m_run + log2f(l_tot)) * LN2;
     }
 }
 

@@ -33,8 +33,12 @@
  *   dout  (B, T, C)   gradient of the loss with respect to out
  *   dqkv  (B, T, 3C)  [dQ | dK | dV], mirrors qkv; overwritten, never
  *                     accumulated into
- *   delta (B, n_head, T) float32 workspace; on return from attn_bwd (once
- *                     the stream has run) it holds D
+ *   delta         float32 workspace of attn_bwd_workspace_floats(B, T, n_head)
+ *                 = 2 * B * n_head * Tp floats, Tp = T rounded up to a multiple
+ *                 of 64: first D[b, h, t] at (b * n_head + h) * Tp + t (0 for
+ *                 t >= T), then LSE * log2(e) at the same offsets plus
+ *                 B * n_head * Tp (+inf for t >= T); written by the backward's
+ *                 preprocess stage and read by its other two stages
  * Element types: the unsuffixed calls take bf16 (IEEE binary32 upper half,
  * passed as void*), accumulate in float32 and round results to nearest-even
  * bf16; the _f32 calls take and produce float32 throughout.
@@ -48,12 +52,11 @@
  * streams may run concurrently as long as their buffers do not overlap.
  *
  * Shapes: head_dim must be 64. B, T and n_head may be any non-negative value
- * whose tensors fit in 2^62 bytes; a call with B, T or n_head equal to 0 has
- * nothing to compute and returns ATTN_OK without touching memory (its
- * pointers may then be NULL). bf16 tensors (qkv, out, dout, dqkv) must start
- * on a 16-byte boundary, float32 tensors on a 4-byte boundary (16 bytes for
- * qkv, out, dout and dqkv of the _f32 calls). Outputs may not overlap inputs
- * or each other.
+ * whose tensors fit in 2^62 bytes and whose launch grids fit in 2^31 - 1
+ * workgroups; a call with B, T or n_head equal to 0 has nothing to compute
+ * and returns ATTN_OK without touching memory (its pointers may then be
+ * NULL). qkv, out, dout, dqkv and delta must start on a 16-byte boundary,
+ * lse on a 4-byte boundary. Outputs may not overlap inputs or each other.
  *
  * Errors: every call returns a status code and never throws. Argument checks
  * run before any HIP call, in this order: NULL pointer, shape, unsupported
@@ -86,30 +89,32 @@ int attn_fwd(const void* qkv, void* out, float* lse,
 /* Backward: dqkv = gradients of sum(dout * out) with respect to qkv, given
  * the out and lse written by attn_fwd for the same qkv. Runs
  * attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq in that order on
- * `stream`; `delta` is the caller's (B, n_head, T) float32 workspace. */
-int attn_bwd(const void* dout, const void* qkv, const void* out,
-             const float* lse, void* dqkv, float* delta,
+ * `stream`; `delta` is the caller's workspace (layout above). */
+int attn_bwd(const void* dout, const void* qkv, const void* out, const float* lse,
+             void* dqkv, float* delta,
              int B, int T, int n_head, int head_dim, void* stream);
 
 /* The three stages of attn_bwd, exported so that each kernel can be launched
  * and timed on its own.
- *   attn_bwd_preprocess: delta[b,h,t] = sum_k dout[b,t,h,k] * out[b,t,h,k]
+ *   attn_bwd_preprocess: D = rowsum(dout * out) and LSE * log2(e) into delta
  *   attn_bwd_dkdv:       writes the dK and dV blocks of dqkv
  *   attn_bwd_dq:         writes the dQ block of dqkv
  * dkdv and dq read delta, so they must follow preprocess on the stream;
  * they write disjoint columns of dqkv and may run in either order. */
-int attn_bwd_preprocess(const void* dout, const void* out, float* delta,
+int attn_bwd_preprocess(const void* dout, const void* out, const float* lse, float* delta,
                         int B, int T, int n_head, int head_dim, void* stream);
-int attn_bwd_dkdv(const void* dout, const void* qkv, const float* lse,
-                  const float* delta, void* dqkv,
+int attn_bwd_dkdv(const void* dout, const void* qkv, const float* delta, void* dqkv,
                   int B, int T, int n_head, int head_dim, void* stream);
-int attn_bwd_dq(const void* dout, const void* qkv, const float* lse,
-                const float* delta, void* dqkv,
+int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqkv,
                 int B, int T, int n_head, int head_dim, void* stream);
+
+/* Number of floats the backward workspace `delta` must hold for this shape:
+ * 2 * B * n_head * round_up(T, 64); -1 if an argument is negative. */
+long long attn_bwd_workspace_floats(int B, int T, int n_head);
 
 /* --------------------------------------------------------------- fp32 ---- */
 
-/* Same operations in float32 storage and arithmetic. */
+/* Same operations in float32 storage and arithmetic (same workspace). */
 int attn_fwd_f32(const float* qkv, float* out, float* lse,
                  int B, int T, int n_head, int head_dim, void* stream);
 int attn_bwd_f32(const float* dout, const float* qkv, const float* out,

@@ -36,14 +36,15 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+long|\w+)\**\s+\**(attn_\w+)\s*\(",
+                                 text, flags=re.M)))
 
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
-              "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "attn_last_error",
-              "attn_version"):
+              "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_workspace_floats",
+              "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
 
@@ -111,12 +112,23 @@ def test_backward_validation(L, fn):
 @no_gpu_only
 def test_stage_validation(L):
     ok = (1, 64, 2, 64)
-    assert L.attn_bwd_preprocess(G, O, None, *ok, None) == -1
-    assert L.attn_bwd_preprocess(G, O, O, *ok, None) == -6
-    assert L.attn_bwd_dkdv(G, Q, LS, DL, None, *ok, None) == -1
-    assert L.attn_bwd_dkdv(G, Q, LS, DL, DQ, 1, 64, 2, 16, None) == -3
-    assert L.attn_bwd_dq(G, Q, LS, DL, Q, *ok, None) == -6
-    assert L.attn_bwd_dq(G, Q, LS, DQ + 32, DQ, *ok, None) == -6  # delta read inside dqkv
+    assert L.attn_bwd_preprocess(G, O, LS, None, *ok, None) == -1
+    assert L.attn_bwd_preprocess(G, O, None, DL, *ok, None) == -1
+    assert L.attn_bwd_preprocess(G, O, LS, O, *ok, None) == -6      # workspace is out
+    assert L.attn_bwd_preprocess(G, O, LS, DL + 4, *ok, None) == -5  # workspace misaligned
+    assert L.attn_bwd_dkdv(G, Q, DL, None, *ok, None) == -1
+    assert L.attn_bwd_dkdv(G, Q, DL, DQ, 1, 64, 2, 16, None) == -3
+    assert L.attn_bwd_dq(G, Q, DL, Q, *ok, None) == -6
+    assert L.attn_bwd_dq(G, Q, DQ + 32, DQ, *ok, None) == -6  # workspace read inside dqkv
+
+
+def test_workspace_size(L):
+    assert L.attn_bwd_workspace_floats(1, 64, 2) == 2 * 2 * 64
+    assert L.attn_bwd_workspace_floats(1, 65, 2) == 2 * 2 * 128
+    assert L.attn_bwd_workspace_floats(16, 1024, 12) == 2 * 16 * 12 * 1024
+    assert L.attn_bwd_workspace_floats(3, 1, 5) == 2 * 3 * 5 * 64
+    assert L.attn_bwd_workspace_floats(0, 10, 2) == 0
+    assert L.attn_bwd_workspace_floats(-1, 10, 2) == -1
 
 
 def test_empty_problems_are_noops(L):
@@ -125,7 +137,8 @@ def test_empty_problems_are_noops(L):
         assert L.attn_fwd_f32(None, None, None, B, T, H, 64, None) == 0
         assert L.attn_bwd(None, None, None, None, None, None, B, T, H, 64, None) == 0
         assert L.attn_bwd_f32(None, None, None, None, None, None, B, T, H, 64, None) == 0
-        assert L.attn_bwd_dkdv(None, None, None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd_dkdv(None, None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd_preprocess(None, None, None, None, B, T, H, 64, None) == 0
 
 
 @no_gpu_only
