@@ -23,6 +23,10 @@
 namespace cattn {
 namespace {
 
+#ifndef CATTN_DKDV_WAVES_PER_SIMD
+#define CATTN_DKDV_WAVES_PER_SIMD 2
+#endif
+
 constexpr int ROW_PAD = 64;
 constexpr int NSTAGE = 3;
 
@@ -94,7 +98,69 @@ struct alignas(16) DkdvSmem {
     float stats[NSTAGE][2 * KV_BM];  // [LSE * log2 e | D] of the tile's queries
 };
 
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
+// One 32-query half (QB) of a query tile for the dK/dV kernel: S and dP on
+// MFMA, P and dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS. MASK
+// applies the causal mask (the tile holding this wave's diagonal only).
+template <int QB, bool MASK>
+__device__ __forceinline__ void dkdv_half(lds_bf16* qt, lds_bf16* gt,
+                                          __attribute__((address_space(3))) const float* stats,
+                                          const bf16x8 (&kreg)[4], const bf16x8 (&vreg)[4],
+                                          const int (&roff)[4], const int (&troff)[2][2],
+                                          f32x16 (&dvt)[2], f32x16 (&dkt)[2], int lim,
+                                          float c_log2, int hf) {
+    typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int o = QB * 32 * 64 + roff[kk];
+        s = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s);
+        dp = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp);
+    }
+    if (MASK) {  // query QB*32 + 8(i/4) + 4hf + (i%4) < my_k - q0  ->  P = 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (QB * 32 + 8 * (i >> 2) + (i & 3) < lim) s[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+        const int qi = QB * 32 + 8 * g4 + 4 * hf;
+        const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(stats + qi);
+        const f32x4 d4 = *reinterpret_cast<lds_f32x4*>(stats + 64 + qi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g4 + r;
+            const float p = fast_exp2(fmaf(s[i], c_log2, -l4[r]));
+            s[i] = p;
+            dp[i] = p * (dp[i] - d4[r]);
+        }
+    }
+    const bf16x8 p0 = c_rows_to_operand(s, 0), p1 = c_rows_to_operand(s, 1);
+    const bf16x8 ds0 = c_rows_to_operand(dp, 0), ds1 = c_rows_to_operand(dp, 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        bf16x8 a[2];
+        atile_tr2<2 * QB>(gt, troff[db][0], troff[db][1], a);
+        dvt[db] = mfma32(a[0], p0, dvt[db]);
+        dvt[db] = mfma32(a[1], p1, dvt[db]);
+        atile_tr2<2 * QB>(qt, troff[db][0], troff[db][1], a);
+        dkt[db] = mfma32(a[0], ds0, dkt[db]);
+        dkt[db] = mfma32(a[1], ds1, dkt[db]);
+    }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
+                                          __attribute__((address_space(3))) const float* stats,
+                                          const bf16x8 (&kreg)[4], const bf16x8 (&vreg)[4],
+                                          const int (&roff)[4], const int (&troff)[2][2],
+                                          f32x16 (&dvt)[2], f32x16 (&dkt)[2], int lim,
+                                          float c_log2, int hf) {
+    dkdv_half<0, MASK>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+    dkdv_half<1, MASK>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+}
+
+__global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
     bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_kt, float c_log2, float scale) {
     __shared__ DkdvSmem sm;
@@ -184,61 +250,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
         lds_bf16* qt = atile_view(sm.q[st]);
         lds_bf16* gt = atile_view(sm.g[st]);
         typedef __attribute__((address_space(3))) const float lds_f32;
-        typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
-        typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
         lds_f32* stats = (lds_f32*)atile_view((const bf16*)sm.stats[st]);
-
-        // S = Q K^T and dP = dO V^T : two 32-query blocks each.
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = zero16();
-            dp[qb] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int o = qb * 32 * 64 + roff[kk];
-                s[qb] = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s[qb]);
-                dp[qb] = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp[qb]);
-            }
-        }
-        // P = exp2(c*s - LSE*log2 e), zero where key > query; dS = P (dP - D).
-        // Only the tile holding this wave's diagonal (q0 == kw rounded down to
-        // 64) has masked entries: query q0 + qi + r < my_k.
-        const bool diag = q0 == (kw & ~(KV_BM - 1));
         const int lim = my_k - q0 - 4 * hf;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int qi = qb * 32 + 8 * g4 + 4 * hf;
-                const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(stats + qi);
-                const f32x4 d4 = *reinterpret_cast<lds_f32x4*>(stats + KV_BM + qi);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 4 * g4 + r;
-                    float p = fast_exp2(fmaf(s[qb][i], c_log2, -l4[r]));
-                    if (diag && qb * 32 + 8 * g4 + r < lim) p = 0.0f;
-                    s[qb][i] = p;
-                    dp[qb][i] = p * (dp[qb][i] - d4[r]);
-                }
-            }
-        bf16x8 pb[4], dsb[4];
-#pragma unroll
-        for (int qc = 0; qc < 4; ++qc) {
-            pb[qc] = c_rows_to_operand(s[qc >> 1], qc & 1);
-            dsb[qc] = c_rows_to_operand(dp[qc >> 1], qc & 1);
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS : K = 64 queries in four chunks.
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            bf16x8 a[4];
-            atile_tr4(gt, troff[db][0], troff[db][1], a);
-#pragma unroll
-            for (int qc = 0; qc < 4; ++qc) dvt[db] = mfma32(a[qc], pb[qc], dvt[db]);
-            atile_tr4(qt, troff[db][0], troff[db][1], a);
-#pragma unroll
-            for (int qc = 0; qc < 4; ++qc) dkt[db] = mfma32(a[qc], dsb[qc], dkt[db]);
-        }
+        if (q0 == (kw & ~(KV_BM - 1)))  // the tile holding this wave's diagonal
+            dkdv_tile<true>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+        else
+            dkdv_tile<false>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
     }
 
     if (my_k < T) {
@@ -275,6 +292,51 @@ struct DqSmem {
     bf16 k[NSTAGE][ATILE_ELEMS];
     bf16 v[NSTAGE][ATILE_ELEMS];
 };
+
+// One 32-key half (KB) of a key tile for the dQ kernel: S^T and dP^T on
+// MFMA, P^T and dS^T on the VALU, then dQ^T += K^T dS^T. MASK applies the
+// causal mask (the tile holding this wave's diagonal only).
+template <int KB, bool MASK>
+__device__ __forceinline__ void dq_half(lds_bf16* kt, lds_bf16* vt, const bf16x8 (&qreg)[4],
+                                        const bf16x8 (&greg)[4], const int (&roff)[4],
+                                        const int (&troff)[2][2], f32x16 (&dqt)[2], int lim,
+                                        float lse2, float dd, float c_log2) {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int o = KB * 32 * 64 + roff[kk];
+        s = mfma32(*reinterpret_cast<lds_bf16x8*>(kt + o), qreg[kk], s);
+        dp = mfma32(*reinterpret_cast<lds_bf16x8*>(vt + o), greg[kk], dp);
+    }
+    if (MASK) {  // key KB*32 + 8(i/4) + 4hf + (i%4) > my_q - k0  ->  P = 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (KB * 32 + 8 * (i >> 2) + (i & 3) > lim) s[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], c_log2, -lse2));
+        dp[i] = p * (dp[i] - dd);
+    }
+    const bf16x8 ds0 = c_rows_to_operand(dp, 0), ds1 = c_rows_to_operand(dp, 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        bf16x8 a[2];
+        atile_tr2<2 * KB>(kt, troff[db][0], troff[db][1], a);
+        dqt[db] = mfma32(a[0], ds0, dqt[db]);
+        dqt[db] = mfma32(a[1], ds1, dqt[db]);
+    }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dq_tile(lds_bf16* kt, lds_bf16* vt, const bf16x8 (&qreg)[4],
+                                        const bf16x8 (&greg)[4], const int (&roff)[4],
+                                        const int (&troff)[2][2], f32x16 (&dqt)[2], int lim,
+                                        float lse2, float dd, float c_log2) {
+    dq_half<0, MASK>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
+    dq_half<1, MASK>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
+}
 
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
@@ -354,42 +416,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
         const int st = j % NSTAGE;
         lds_bf16* kt = atile_view(sm.k[st]);
         lds_bf16* vt = atile_view(sm.v[st]);
-        typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = zero16();
-            dp[kb] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int o = kb * 32 * 64 + roff[kk];
-                s[kb] = mfma32(*reinterpret_cast<lds_bf16x8*>(kt + o), qreg[kk], s[kb]);
-                dp[kb] = mfma32(*reinterpret_cast<lds_bf16x8*>(vt + o), greg[kk], dp[kb]);
-            }
-        }
-        // Only the tile holding this wave's diagonal (k0 == qw rounded down
-        // to 64) has masked entries: key k0 + kb*32 + 8(i/4) + 4hf + (i%4) > my_q.
-        const bool diag = k0 == (qw & ~(DQ_BN - 1));
         const int lim = my_q - k0 - 4 * hf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float p = fast_exp2(fmaf(s[kb][i], c_log2, -lse2));
-                if (diag && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.0f;
-                dp[kb][i] = p * (dp[kb][i] - dd);
-            }
-        bf16x8 dsb[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) dsb[kc] = c_rows_to_operand(dp[kc >> 1], kc & 1);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            bf16x8 a[4];
-            atile_tr4(kt, troff[db][0], troff[db][1], a);
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) dqt[db] = mfma32(a[kc], dsb[kc], dqt[db]);
-        }
+        if (k0 == (qw & ~(DQ_BN - 1)))  // the tile holding this wave's diagonal
+            dq_tile<true>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
+        else
+            dq_tile<false>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
     }
 
     if (q_ok) {

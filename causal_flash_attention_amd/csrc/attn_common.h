@@ -245,6 +245,26 @@ __device__ __forceinline__ void atile_tr4(lds_bf16* tile, int off0, int off1, bf
     }
 }
 
+// Two consecutive chunks (KC0, KC0 + 1) of the operands read by atile_tr4.
+template <int KC0>
+__device__ __forceinline__ void atile_tr2(lds_bf16* tile, int off0, int off1, bf16x8 out[2]) {
+    const unsigned int a0 = (unsigned int)(uintptr_t)(tile + off0);
+    const unsigned int a1 = (unsigned int)(uintptr_t)(tile + off1);
+    u32x2 r0, r1, r2, r3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "i"(KC0 * 2048), "i"((KC0 + 1) * 2048));
+    const u32x4 v0 = {r0[0], r0[1], r1[0], r1[1]};
+    const u32x4 v1 = {r2[0], r2[1], r3[0], r3[1]};
+    out[0] = as_bf16x8(v0);
+    out[1] = as_bf16x8(v1);
+}
+
 // Wait until at most n of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {

@@ -24,7 +24,7 @@
 #include "attn_common.h"
 
 #ifndef CATTN_FWD_QB
-#define CATTN_FWD_QB 2
+#define CATTN_FWD_QB 1
 #endif
 
 namespace cattn {

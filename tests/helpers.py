@@ -102,10 +102,19 @@ def compare(gpu: dict, ref: dict, heads, n_head: int, head_dim: int = 64) -> dic
     return m
 
 
-def assert_parity(m: dict, dtype: str, label: str) -> None:
+def bf16_o_bound(o_refmax: float) -> float:
+    """O bar for bf16 stress inputs whose outputs exceed the unit scale of the
+    workloads: a near one-hot softmax makes O one V row, whose error is then
+    its output rounding (<= |O| 2^-9) plus the rounding of the dominant bf16
+    weight (<= |O| 2^-9), so 2^-7 |O|max leaves a factor 2 of headroom. It
+    never drops below the workloads' 1e-2."""
+    return max(BF16_O_MAXABS, o_refmax * 2.0 ** -7)
+
+
+def assert_parity(m: dict, dtype: str, label: str, o_bound: float = BF16_O_MAXABS) -> None:
     log(f"[parity] {label}: " + ", ".join(f"{k}={v:.3e}" for k, v in sorted(m.items())))
     if dtype == "bf16":
-        assert m["o_maxabs"] <= BF16_O_MAXABS, (label, m)
+        assert m["o_maxabs"] <= o_bound, (label, m)
         assert m["lse_maxabs"] <= BF16_LSE_MAXABS, (label, m)
         for k in ("dq", "dk", "dv"):
             assert m[f"{k}_rel_l2"] <= BF16_GRAD_REL_L2, (label, k, m)

@@ -12,7 +12,8 @@ import oracle
 from causal_flash_attention_amd import inputs as I
 from causal_flash_attention_amd.workloads import WORKLOADS
 
-from helpers import assert_parity, compare, log, run_library, sample_heads, to_device, to_host64
+from helpers import (BF16_O_MAXABS, assert_parity, bf16_o_bound, compare, log, run_library,
+                     sample_heads, to_device, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +28,8 @@ def _scale_qk(qkv, dtype, H, gain):
     return I.f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
-def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", qk_gain=1.0):
+def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", qk_gain=1.0,
+                stress=False):
     log(f"[case] {label} B={B} T={T} H={H} dtype={dtype} seed={seed} qk_gain={qk_gain}")
     qkv, dout = I.attention_inputs(B, T, H, D, dtype, qkv_std, dout_std, seed=seed)
     if qk_gain != 1.0:
@@ -44,7 +46,8 @@ def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", q
     m = compare(gpu, ref, heads, H, D)
     for k in ("out", "lse", "dqkv"):
         assert np.all(np.isfinite(gpu[k])), (label, k)
-    assert_parity(m, dtype, f"{label} B={B} T={T} H={H} {dtype}")
+    o_bound = bf16_o_bound(m["o_refmax"]) if stress else BF16_O_MAXABS
+    assert_parity(m, dtype, f"{label} B={B} T={T} H={H} {dtype}", o_bound)
     return m
 
 
@@ -88,7 +91,7 @@ def test_long_sequence_bf16():
 def test_peaky_scores_bf16():
     # Q and K scaled by 4: logits with a standard deviation of 16, so the
     # running max moves often and most probabilities underflow.
-    _check_case(2, 300, 2, "bf16", 1.0, 0.01, seed=11, label="peaky", qk_gain=4.0)
+    _check_case(2, 300, 2, "bf16", 1.0, 0.01, seed=11, label="peaky", qk_gain=4.0, stress=True)
 
 
 def test_peaky_scores_f32():
