@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
             }
         }
         float mt[FWD_QB];
-        bool grow = false;
+        bool grow[FWD_QB], any_grow = false;
 #pragma unroll
         for (int qb = 0; qb < FWD_QB; ++qb) {
             float mx = s[qb][0][0];
@@ -164,13 +164,17 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
             mx = fmaxf(mx, swap_halves(mx));
             mt[qb] = mx * c_log2;
-            grow |= mt[qb] > m_run[qb] + RESCALE_LOG2;
+            grow[qb] = mt[qb] > m_run[qb] + RESCALE_LOG2;
+            any_grow |= grow[qb];
         }
-        if (__any(grow)) {
+        // Each row decides for itself (rows that do not grow keep their max
+        // and scale by exactly 1), so a row's arithmetic never depends on the
+        // other rows of the wave: later tokens cannot change earlier rows.
+        if (__any(any_grow)) {
 #pragma unroll
             for (int qb = 0; qb < FWD_QB; ++qb) {
-                const float m_new = fmaxf(m_run[qb], mt[qb]);
-                const float alpha = fast_exp2(m_run[qb] - m_new);
+                const float m_new = grow[qb] ? mt[qb] : m_run[qb];
+                const float alpha = grow[qb] ? fast_exp2(m_run[qb] - m_new) : 1.0f;
                 l_run[qb] *= alpha;
                 m_run[qb] = m_new;
 #pragma unroll
