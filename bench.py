@@ -61,6 +61,14 @@ def parse_args(argv=None):
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run a plain 256 MiB device copy (for counter scaling)")
+    p.add_argument("--write-profiles", action="store_true",
+                   help="summarise rocprofv3 CSV output (--trace-dir, --fetch-dir, --write-dir) "
+                        "into profiles/ and exit")
+    p.add_argument("--trace-dir", default=None)
+    p.add_argument("--fetch-dir", default=None)
+    p.add_argument("--write-dir", default=None)
+    p.add_argument("--profile-command", default="",
+                   help="the commands that produced the CSVs, recorded in the summaries")
     return p.parse_args(argv)
 
 
@@ -86,6 +94,87 @@ def traffic_from_profile(kernel: str, workload: str):
     if m_src.group(1) != source_digest(os.path.join(CSRC, KERNELS[kernel][0])):
         return None
     return float(m_val.group(1))
+
+
+COPY_BYTES = 256 << 20  # the --copy-calibration copy
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _kernel_of(name: str):
+    for k, tag in (("attn_fwd", "attn_fwd_bf16_kernel"), ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
+                   ("attn_bwd_dkdv", "attn_bwd_dkdv_bf16_kernel"), ("attn_bwd_dq", "attn_bwd_dq_bf16_kernel")):
+        if tag in name:
+            return k
+    if "copyBuffer" in name or "copy" in name.lower():
+        return "copy"
+    return None
+
+
+def _counter_means(d: str, counter: str):
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        k = _kernel_of(r.get("Kernel_Name", ""))
+        if k:
+            per.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def write_profiles(args, w) -> int:
+    """Turn rocprofv3 CSV output into the text summaries under profiles/."""
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    cmd = args.profile_command or "(see the bench.py --write-profiles invocation)"
+    if args.trace_dir:
+        rows = _csv_rows(args.trace_dir, "kernel_stats.csv")
+        lines = [f"# rocprofv3 kernel-trace statistics, workload {w.name}",
+                 f"# command: {cmd}",
+                 "# kernel, calls, average_us, min_us, max_us, share_percent"]
+        for r in rows:
+            k = _kernel_of(r["Name"]) or r["Name"][:60]
+            lines.append(f"{k}, {r['Calls']}, {float(r['AverageNs']) / 1e3:.2f}, "
+                         f"{float(r['MinNs']) / 1e3:.2f}, {float(r['MaxNs']) / 1e3:.2f}, "
+                         f"{float(r['Percentage']):.2f}")
+        path = os.path.join(PROFILE_DIR, f"kernel_stats_{w.name}.txt")
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(path)
+    if args.fetch_dir and args.write_dir:
+        fetch = _counter_means(args.fetch_dir, "FETCH_SIZE")
+        write = _counter_means(args.write_dir, "WRITE_SIZE")
+        if "copy" not in fetch or "copy" not in write:
+            raise SystemExit("the counter runs need --copy-calibration (a plain copy of known size)")
+        f_fetch = COPY_BYTES / (fetch["copy"] * 1024.0)
+        f_write = COPY_BYTES / (write["copy"] * 1024.0)
+        for k in KERNELS:
+            if k not in fetch or k not in write:
+                continue
+            traffic = fetch[k] * 1024.0 * f_fetch + write[k] * 1024.0 * f_write
+            text = "\n".join([
+                f"# HBM traffic of {k} on workload {w.name}, from rocprofv3 counters",
+                f"# command: {cmd}",
+                f"source_sha256_16: {source_digest(os.path.join(CSRC, KERNELS[k][0]))}",
+                f"fetch_kib_per_dispatch: {fetch[k]:.1f}",
+                f"write_kib_per_dispatch: {write[k]:.1f}",
+                f"copy_calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE "
+                f"{fetch['copy']:.1f} KiB and WRITE_SIZE {write['copy']:.1f} KiB per dispatch; "
+                f"scale factors fetch {f_fetch:.4f}, write {f_write:.4f}",
+                f"traffic_bytes_per_launch: {traffic:.6e}",
+            ]) + "\n"
+            path = os.path.join(PROFILE_DIR, f"{k}_{w.name}_hbm_traffic.txt")
+            with open(path, "w") as fh:
+                fh.write(text)
+            print(path)
+    return 0
 
 
 def cpu_baseline(w, target_s: float):
@@ -138,14 +227,18 @@ def main(argv=None):
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    from causal_flash_attention_amd.workloads import BY_NAME, HEADLINE
+
+    w = BY_NAME[args.workload] if args.workload else HEADLINE
+    if args.write_profiles:
+        return write_profiles(args, w)
+
     import numpy as np
     import torch
 
     from causal_flash_attention_amd import binding
     from causal_flash_attention_amd import inputs as I
-    from causal_flash_attention_amd.workloads import BY_NAME, HEADLINE
 
-    w = BY_NAME[args.workload] if args.workload else HEADLINE
     if w.dtype != "bf16":
         raise SystemExit("the bench times the bf16 path")
     if not torch.cuda.is_available():
