@@ -139,13 +139,10 @@ __device__ __forceinline__ void dkdv_half(lds_bf16* qt, lds_bf16* gt,
     const bf16x8 ds0 = c_rows_to_operand(dp, 0), ds1 = c_rows_to_operand(dp, 1);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        bf16x8 a[2];
-        atile_tr2<2 * QB>(gt, troff[db][0], troff[db][1], a);
-        dvt[db] = mfma32(a[0], p0, dvt[db]);
-        dvt[db] = mfma32(a[1], p1, dvt[db]);
-        atile_tr2<2 * QB>(qt, troff[db][0], troff[db][1], a);
-        dkt[db] = mfma32(a[0], ds0, dkt[db]);
-        dkt[db] = mfma32(a[1], ds1, dkt[db]);
+        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB), p0, dvt[db]);
+        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB + 1), p1, dvt[db]);
+        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB), ds0, dkt[db]);
+        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB + 1), ds1, dkt[db]);
     }
 }
 
@@ -192,19 +189,6 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const int kw = k0 + wave * 32;
     const int my_k = kw + l32;
 
-    // K and V of this lane's key as B operands (of S = Q K^T and dP = dO V^T).
-    bf16x8 kreg[4], vreg[4];
-    {
-        const bool ok = my_k < T;
-        const bf16* kp = kbase + (long long)my_k * rs + hf * 8;
-        const bf16* vp = vbase + (long long)my_k * rs + hf * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            kreg[kk] = as_bf16x8(load16(kp + kk * 16, ok));
-            vreg[kk] = as_bf16x8(load16(vp + kk * 16, ok));
-        }
-    }
-
     // Per-lane LDS offsets: row-major reads of rows qb*32 + l32, chunks 2kk + hf;
     // transposed reads for d blocks 0 and 1.
     int roff[4];
@@ -228,12 +212,27 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
         atile_load(sm.g[st], gbase, C, q0, T, wave, lane);
         if (wave == 0 && lane < 32) {
             const float* src = (lane < 16 ? lse2_row : dd_row) + q0 + 4 * (lane & 15);
-            __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)sm.stats[st], 16, 0, 0);
+            lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(sm.stats[st])));
         }
     };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
         if (j < n_it) issue(j, j);
+
+    // K and V of this lane's key as B operands (of S = Q K^T and dP = dO V^T).
+    bf16x8 kreg[4], vreg[4];
+    {
+        const bool ok = my_k < T;
+        const bf16* kp = kbase + (long long)my_k * rs + hf * 8;
+        const bf16* vp = vbase + (long long)my_k * rs + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kreg[kk] = as_bf16x8(load16(kp + kk * 16, ok));
+            vreg[kk] = as_bf16x8(load16(vp + kk * 16, ok));
+        }
+    }
+    // The first tiles and K, V land before the loop (no waits on K, V inside it).
+    wait_vmem<0>();
 
     for (int it = 0; it < n_it; ++it) {
         if (it + 1 < n_it) {
@@ -322,10 +321,8 @@ __device__ __forceinline__ void dq_half(lds_bf16* kt, lds_bf16* vt, const bf16x8
     const bf16x8 ds0 = c_rows_to_operand(dp, 0), ds1 = c_rows_to_operand(dp, 1);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        bf16x8 a[2];
-        atile_tr2<2 * KB>(kt, troff[db][0], troff[db][1], a);
-        dqt[db] = mfma32(a[0], ds0, dqt[db]);
-        dqt[db] = mfma32(a[1], ds1, dqt[db]);
+        dqt[db] = mfma32(atile_tr(kt, troff[db][0], troff[db][1], 2 * KB), ds0, dqt[db]);
+        dqt[db] = mfma32(atile_tr(kt, troff[db][0], troff[db][1], 2 * KB + 1), ds1, dqt[db]);
     }
 }
 
@@ -369,20 +366,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const int my_q = qw + l32;
     const bool q_ok = my_q < T;
 
-    bf16x8 qreg[4], greg[4];
-    {
-        const bf16* qp = qbase + (long long)my_q * rs + hf * 8;
-        const bf16* gp = gbase + (long long)my_q * C + hf * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            qreg[kk] = as_bf16x8(load16(qp + kk * 16, q_ok));
-            greg[kk] = as_bf16x8(load16(gp + kk * 16, q_ok));
-        }
-    }
-    const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
-    const float dd = q_ok ? ws[ws_i] : 0.0f;
-    const float lse2 = q_ok ? ws[(long long)BH * Tp + ws_i] : INFINITY;
-
     int roff[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) roff[kk] = l32 * 64 + (((2 * kk + hf) ^ swz(l32)) << 3);
@@ -401,6 +384,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
             atile_load(sm.k[j], kbase, rs, j * DQ_BN, T, wave, lane);
             atile_load(sm.v[j], vbase, rs, j * DQ_BN, T, wave, lane);
         }
+
+    bf16x8 qreg[4], greg[4];
+    {
+        const bf16* qp = qbase + (long long)my_q * rs + hf * 8;
+        const bf16* gp = gbase + (long long)my_q * C + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            qreg[kk] = as_bf16x8(load16(qp + kk * 16, q_ok));
+            greg[kk] = as_bf16x8(load16(gp + kk * 16, q_ok));
+        }
+    }
+    const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
+    const float dd = q_ok ? ws[ws_i] : 0.0f;
+    const float lse2 = q_ok ? ws[(long long)BH * Tp + ws_i] : INFINITY;
+    // The first tiles and this lane's Q, dO, LSE, D land before the loop.
+    wait_vmem<0>();
 
     for (int j = 0; j < n_kt; ++j) {
         if (j + 1 < n_kt) wait_vmem<4>();

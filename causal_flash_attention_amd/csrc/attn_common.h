@@ -164,6 +164,23 @@ __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// One direct global->LDS load: 16 bytes from `g` (per lane) to LDS address
+// m0 + 16 * lane. Issued from asm so that the compiler does not track it as
+// a pending LDS write: otherwise it waits for every such load before each
+// transposing LDS read, which would drain the prefetch pipeline. The
+// instruction has no output registers; ordering against the readers comes
+// from explicit vmcnt waits (wait_vmem) and the workgroup barrier.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned int lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned int lds_addr(const void* p) {
+    return (unsigned int)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // Issue the loads of rows [r0, r0 + 64) of a strided bf16 matrix into an LDS
 // tile; rows past `nrows` repeat row nrows - 1 (callers mask them). Wave w
 // (of 4) loads tile rows 16w .. 16w + 15: two instructions, each writing 8
@@ -176,7 +193,8 @@ __device__ __forceinline__ void atile_load(bf16* tile, const bf16* base, long lo
         const int c = (lane & 7) ^ swz(tr);
         const int row = min(r0 + tr, nrows - 1);
         const bf16* g = base + (long long)row * row_stride + c * 8;
-        __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(tile + (16 * wave + 8 * i) * 64), 16, 0, 0);
+        const unsigned int dst = __builtin_amdgcn_readfirstlane(lds_addr(tile + (16 * wave + 8 * i) * 64));
+        lds_dma16(g, dst);
     }
 }
 
@@ -214,6 +232,18 @@ __device__ __forceinline__ void atile_tr_offsets(int lane, int db, int* off0, in
     const int r0 = 4 * h + (i >> 2), r1 = r0 + 8;
     *off0 = r0 * 64 + (((d >> 3) ^ swz(r0)) << 3) + (d & 7);
     *off1 = r1 * 64 + (((d >> 3) ^ swz(r1)) << 3) + (d & 7);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// A operand X^T of chunk kc through the transposing-read intrinsic: the
+// compiler tracks these reads and waits for each only where it is used.
+__device__ __forceinline__ bf16x8 atile_tr(lds_bf16* tile, int off0, int off1, int kc) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + kc * 16 * 64 + off0));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + kc * 16 * 64 + off1));
+    const i16x4 v[2] = {a, b};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // The four A operands X^T of one d block (kc = 0..3) in one go: eight

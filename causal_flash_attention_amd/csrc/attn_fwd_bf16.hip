@@ -73,16 +73,6 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
     const int q0 = qt * FWD_BM;
     const int qw = q0 + wave * 32 * FWD_QB;  // first query of this wave
 
-    // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of each block's query.
-    bf16x8 qreg[FWD_QB][4];
-#pragma unroll
-    for (int qb = 0; qb < FWD_QB; ++qb) {
-        const int q = qw + 32 * qb + l32;
-        const bf16* p = qbase + (long long)q * rs + hf * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qreg[qb][kk] = as_bf16x8(load16(p + kk * 16, q < T));
-    }
-
     const int kend = min(q0 + FWD_BM, T);
     const int n_kt = (kend + FWD_BN - 1) / FWD_BN;
 
@@ -109,6 +99,19 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
             atile_load(sm.k[j], kbase, rs, j * FWD_BN, T, wave, lane);
             atile_load(sm.v[j], vbase, rs, j * FWD_BN, T, wave, lane);
         }
+
+    // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of each block's query.
+    bf16x8 qreg[FWD_QB][4];
+#pragma unroll
+    for (int qb = 0; qb < FWD_QB; ++qb) {
+        const int q = qw + 32 * qb + l32;
+        const bf16* p = qbase + (long long)q * rs + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qreg[qb][kk] = as_bf16x8(load16(p + kk * 16, q < T));
+    }
+    // Everything issued so far (the first tiles and Q) lands before the loop,
+    // so the compiler needs no waits on Q inside it.
+    wait_vmem<0>();
 
     for (int j = 0; j < n_kt; ++j) {
         // Tile j has landed once at most the next tile's loads are pending.
@@ -201,14 +204,13 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
         }
         // O^T += V^T P^T over four 16-key chunks; each V^T operand feeds QB MFMAs.
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            bf16x8 a[4];
-            atile_tr4(vt, voff[db][0], voff[db][1], a);
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x8 a = atile_tr(vt, voff[db][0], voff[db][1], kc);
 #pragma unroll
-                for (int qb = 0; qb < FWD_QB; ++qb) acc[qb][db] = mfma32(a[kc], pb[qb][kc], acc[qb][db]);
-        }
+                for (int qb = 0; qb < FWD_QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][kc], acc[qb][db]);
+            }
     }
 
     // Epilogue: O = acc / l (rounded to bf16), LSE = ln 2 * (m + log2 l).
