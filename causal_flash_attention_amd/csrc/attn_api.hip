@@ -51,6 +51,8 @@ bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi;
 
 // Shape checks shared by every entry point. Sets *empty when there is
 // nothing to compute.
+constexpr long long kMaxChannels = 1LL << 23;  // 64 rows * 3C * 2 bytes < 2^32
+
 int check_shape(int B, int T, int H, int d, int elem, bool* empty) {
     if (B < 0 || T < 0 || H < 0 || d <= 0) return fail(ATTN_ERR_BAD_SHAPE, "B, T, n_head must be >= 0 and head_dim > 0");
     if (d != kHeadDim) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64");
@@ -67,7 +69,8 @@ int check_shape(int B, int T, int H, int d, int elem, bool* empty) {
     const long long tp = ((long long)T + 63) / 64 * 64;
     if (((long long)B * T * H + 15) / 16 + ((long long)B * H * tp + 255) / 256 > kMaxBlocks)
         return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
-    if ((long long)H * d > 0x7fffffffLL / 3) return fail(ATTN_ERR_TOO_LARGE, "3*n_head*head_dim overflows int");
+    // Tile loads address 64 packed qkv rows with 32-bit byte offsets.
+    if ((long long)H * d > kMaxChannels) return fail(ATTN_ERR_TOO_LARGE, "n_head*head_dim exceeds 2^23");
     return ATTN_OK;
 }
 

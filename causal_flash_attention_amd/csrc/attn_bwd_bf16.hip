@@ -18,6 +18,8 @@
 // Workspace (float32, per (batch, head) row padded to Tp = round_up(T, 64)):
 //   ws[0 .. BH*Tp)       D,            0 for t >= T
 //   ws[BH*Tp .. 2*BH*Tp) LSE * log2 e, +inf for t >= T (so P = 0 there)
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace cattn {
@@ -98,25 +100,32 @@ struct alignas(16) DkdvSmem {
     float stats[NSTAGE][2 * KV_BM];  // [LSE * log2 e | D] of the tile's queries
 };
 
-// One 32-query half (QB) of a query tile for the dK/dV kernel: S and dP on
-// MFMA, P and dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS. MASK
-// applies the causal mask (the tile holding this wave's diagonal only).
-template <int QB, bool MASK>
-__device__ __forceinline__ void dkdv_half(lds_bf16* qt, lds_bf16* gt,
-                                          __attribute__((address_space(3))) const float* stats,
-                                          const bf16x8 (&kreg)[4], const bf16x8 (&vreg)[4],
-                                          const int (&roff)[4], const int (&troff)[2][2],
-                                          f32x16 (&dvt)[2], f32x16 (&dkt)[2], int lim,
-                                          float c_log2, int hf) {
-    typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+// The dK/dV step on a 64-query tile runs as two 32-query halves (QB), each
+// in three phases: S and dP on MFMA; P and dS on the VALU; then
+// dV^T += dO^T P and dK^T += Q^T dS on MFMA. The phases are ordered so that
+// one half's VALU work sits between MFMAs of the other half that do not
+// depend on it. MASK applies the causal mask (the tile holding this wave's
+// diagonal only).
+template <int QB>
+__device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, const bf16x8 (&kreg)[4],
+                                         const bf16x8 (&vreg)[4], const int (&roff)[4],
+                                         f32x16& s, f32x16& dp) {
     typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-    f32x16 s = zero16(), dp = zero16();
+    s = zero16();
+    dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int o = QB * 32 * 64 + roff[kk];
         s = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s);
         dp = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp);
     }
+}
+
+template <int QB, bool MASK>
+__device__ __forceinline__ void dkdv_pds(__attribute__((address_space(3))) const float* stats,
+                                         f32x16& s, f32x16& dp, int lim, float c_log2, int hf,
+                                         bf16x8 (&pds)[4]) {
+    typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
     if (MASK) {  // query QB*32 + 8(i/4) + 4hf + (i%4) < my_k - q0  ->  P = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -135,16 +144,28 @@ __device__ __forceinline__ void dkdv_half(lds_bf16* qt, lds_bf16* gt,
             dp[i] = p * (dp[i] - d4[r]);
         }
     }
-    const bf16x8 p0 = c_rows_to_operand(s, 0), p1 = c_rows_to_operand(s, 1);
-    const bf16x8 ds0 = c_rows_to_operand(dp, 0), ds1 = c_rows_to_operand(dp, 1);
+    pds[0] = c_rows_to_operand(s, 0);
+    pds[1] = c_rows_to_operand(s, 1);
+    pds[2] = c_rows_to_operand(dp, 0);
+    pds[3] = c_rows_to_operand(dp, 1);
+}
+
+template <int QB>
+__device__ __forceinline__ void dkdv_acc(lds_bf16* qt, lds_bf16* gt, const int (&troff)[2][2],
+                                         const bf16x8 (&pds)[4], f32x16 (&dvt)[2],
+                                         f32x16 (&dkt)[2]) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB), p0, dvt[db]);
-        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB + 1), p1, dvt[db]);
-        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB), ds0, dkt[db]);
-        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB + 1), ds1, dkt[db]);
+        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB), pds[0], dvt[db]);
+        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB + 1), pds[1], dvt[db]);
+        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB), pds[2], dkt[db]);
+        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB + 1), pds[3], dkt[db]);
     }
 }
+
+#ifndef CATTN_DKDV_SCHED
+#define CATTN_DKDV_SCHED 0
+#endif
 
 template <bool MASK>
 __device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
@@ -153,15 +174,31 @@ __device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
                                           const int (&roff)[4], const int (&troff)[2][2],
                                           f32x16 (&dvt)[2], f32x16 (&dkt)[2], int lim,
                                           float c_log2, int hf) {
-    dkdv_half<0, MASK>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
-    dkdv_half<1, MASK>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pds0[4], pds1[4];
+    dkdv_sdp<0>(qt, gt, kreg, vreg, roff, s0, dp0);
+    dkdv_sdp<1>(qt, gt, kreg, vreg, roff, s1, dp1);
+    dkdv_pds<0, MASK>(stats, s0, dp0, lim, c_log2, hf, pds0);
+    dkdv_acc<0>(qt, gt, troff, pds0, dvt, dkt);
+    dkdv_pds<1, MASK>(stats, s1, dp1, lim, c_log2, hf, pds1);
+    dkdv_acc<1>(qt, gt, troff, pds1, dvt, dkt);
+#if CATTN_DKDV_SCHED == 1
+    __builtin_amdgcn_iglp_opt(0);
+#elif CATTN_DKDV_SCHED == 2
+    __builtin_amdgcn_iglp_opt(1);
+#elif CATTN_DKDV_SCHED == 3
+    __builtin_amdgcn_iglp_opt(2);
+#elif CATTN_DKDV_SCHED == 4
+    __builtin_amdgcn_iglp_opt(3);
+#endif
 }
 
 __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
     bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_kt, float c_log2, float scale) {
     __shared__ DkdvSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
 
     const int BH = B * H;
@@ -178,6 +215,8 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const int b = bh / H, h = bh - b * H;
     const int C = H * HEAD_DIM;
     const long long rs = 3LL * C;
+    const TileLoader ld_rs = tile_loader(rs, wave, lane);
+    const TileLoader ld_C = tile_loader(C, wave, lane);
     const bf16* qbase = qkv + (long long)b * T * rs + h * HEAD_DIM;
     const bf16* kbase = qbase + C;
     const bf16* vbase = qbase + 2 * C;
@@ -204,16 +243,14 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const int qt_begin = k0 / KV_BM;
     const int n_it = (T + KV_BM - 1) / KV_BM - qt_begin;
 
+    const float* stats_src = (lane < 16 ? lse2_row : dd_row) + 4 * (lane & 15);
     // Issue the loads of query tile `it` (relative) into stage `st`: Q and dO
     // by every wave, the row statistics by wave 0 (lanes 0..31, 16 bytes each).
     auto issue = [&](int it, int st) {
         const int q0 = (qt_begin + it) * KV_BM;
-        atile_load(sm.q[st], qbase, rs, q0, T, wave, lane);
-        atile_load(sm.g[st], gbase, C, q0, T, wave, lane);
-        if (wave == 0 && lane < 32) {
-            const float* src = (lane < 16 ? lse2_row : dd_row) + q0 + 4 * (lane & 15);
-            lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(sm.stats[st])));
-        }
+        atile_load(atile_addr(sm.q[st]), rows_rsrc(qbase, rs, q0, T), 0, ld_rs);
+        atile_load(atile_addr(sm.g[st]), rows_rsrc(gbase, C, q0, T), 0, ld_C);
+        if (wave == 0 && lane < 32) lds_dma16(stats_src + q0, atile_addr((const bf16*)sm.stats[st]));
     };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
@@ -234,7 +271,13 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     // The first tiles and K, V land before the loop (no waits on K, V inside it).
     wait_vmem<0>();
 
-    for (int it = 0; it < n_it; ++it) {
+    // One query tile: wait for its loads, refill the ring, then the tile's
+    // work. Only the first two tiles of a workgroup can precede a wave's keys
+    // or hold its diagonal (keys are 128-aligned, query tiles 64 rows), so the
+    // later tiles run in a loop of their own with no masking branch, which
+    // keeps the accumulators in the same registers from tile to tile.
+    static_assert(KV_BN == 2 * KV_BM, "diagonal within the first two tiles");
+    auto step = [&](int it, auto maybe_diag) {
         if (it + 1 < n_it) {
             if (wave == 0) wait_vmem<5>();
             else wait_vmem<4>();
@@ -244,18 +287,24 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
         __syncthreads();
         if (it + NSTAGE - 1 < n_it) issue(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
         const int q0 = (qt_begin + it) * KV_BM;
-        if (q0 + KV_BM - 1 < kw) continue;  // every query of the tile precedes this wave's keys
         const int st = it % NSTAGE;
         lds_bf16* qt = atile_view(sm.q[st]);
         lds_bf16* gt = atile_view(sm.g[st]);
         typedef __attribute__((address_space(3))) const float lds_f32;
         lds_f32* stats = (lds_f32*)atile_view((const bf16*)sm.stats[st]);
         const int lim = my_k - q0 - 4 * hf;
-        if (q0 == (kw & ~(KV_BM - 1)))  // the tile holding this wave's diagonal
-            dkdv_tile<true>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
-        else
-            dkdv_tile<false>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
-    }
+        if (decltype(maybe_diag)::value) {
+            if (q0 + KV_BM - 1 < kw) return;  // every query of the tile precedes this wave's keys
+            if (q0 == (kw & ~(KV_BM - 1))) {  // the tile holding this wave's diagonal
+                dkdv_tile<true>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+                return;
+            }
+        }
+        dkdv_tile<false>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+    };
+    const int n_head_it = n_it < 2 ? n_it : 2;
+    for (int it = 0; it < n_head_it; ++it) step(it, std::true_type());
+    for (int it = n_head_it; it < n_it; ++it) step(it, std::false_type());
 
     if (my_k < T) {
         bf16* dkp = dqkv + ((long long)b * T + my_k) * rs + C + h * HEAD_DIM;
@@ -339,7 +388,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
     bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_qt, float c_log2, float scale) {
     __shared__ DqSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
 
     const int BH = B * H;
@@ -356,9 +406,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const int b = bh / H, h = bh - b * H;
     const int C = H * HEAD_DIM;
     const long long rs = 3LL * C;
+    const TileLoader ld_rs = tile_loader(rs, wave, lane);
     const bf16* qbase = qkv + (long long)b * T * rs + h * HEAD_DIM;
     const bf16* kbase = qbase + C;
-    const bf16* vbase = qbase + 2 * C;
     const bf16* gbase = dout + (long long)b * T * C + h * HEAD_DIM;
 
     const int q0 = qt * DQ_BM;
@@ -378,12 +428,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const int kend = min(q0 + DQ_BM, T);
     const int n_kt = (kend + DQ_BN - 1) / DQ_BN;
 
+    // K and V rows [k0, k0 + 64) into stage st: one descriptor, since V sits
+    // C elements after K in every packed row.
+    auto issue = [&](int k0, int st) {
+        const i32x4 kv = rows_rsrc(kbase, rs, k0, T);
+        atile_load(atile_addr(sm.k[st]), kv, 0, ld_rs);
+        atile_load(atile_addr(sm.v[st]), kv, 2u * C, ld_rs);
+    };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < n_kt) {
-            atile_load(sm.k[j], kbase, rs, j * DQ_BN, T, wave, lane);
-            atile_load(sm.v[j], vbase, rs, j * DQ_BN, T, wave, lane);
-        }
+        if (j < n_kt) issue(j * DQ_BN, j);
 
     bf16x8 qreg[4], greg[4];
     {
@@ -405,11 +459,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
         if (j + 1 < n_kt) wait_vmem<4>();
         else wait_vmem<0>();
         __syncthreads();
-        if (j + NSTAGE - 1 < n_kt) {
-            const int st = (j + NSTAGE - 1) % NSTAGE;
-            atile_load(sm.k[st], kbase, rs, (j + NSTAGE - 1) * DQ_BN, T, wave, lane);
-            atile_load(sm.v[st], vbase, rs, (j + NSTAGE - 1) * DQ_BN, T, wave, lane);
-        }
+        if (j + NSTAGE - 1 < n_kt) issue((j + NSTAGE - 1) * DQ_BN, (j + NSTAGE - 1) % NSTAGE);
         const int k0 = j * DQ_BN;
         if (k0 > qw + 31) continue;  // whole tile after this wave's queries
         const int st = j % NSTAGE;

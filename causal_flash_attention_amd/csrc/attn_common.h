@@ -181,21 +181,78 @@ __device__ __forceinline__ unsigned int lds_addr(const void* p) {
     return (unsigned int)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// Issue the loads of rows [r0, r0 + 64) of a strided bf16 matrix into an LDS
-// tile; rows past `nrows` repeat row nrows - 1 (callers mask them). Wave w
-// (of 4) loads tile rows 16w .. 16w + 15: two instructions, each writing 8
-// whole rows (1 KB) at lane-contiguous LDS addresses.
-__device__ __forceinline__ void atile_load(bf16* tile, const bf16* base, long long row_stride,
-                                           int r0, int nrows, int wave, int lane) {
+// Raw buffer descriptor (stride 0, 32-bit data format) over `num_bytes`
+// bytes at `base`: buffer loads at byte offsets past num_bytes return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, unsigned int num_bytes) {
+    const unsigned long long p = (unsigned long long)(uintptr_t)base;
+    i32x4 r;
+    r.x = (int)(unsigned int)p;
+    r.y = (int)((unsigned int)(p >> 32) & 0xffffu);
+    r.z = (int)num_bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
+// One direct buffer->LDS load: 16 bytes per lane from byte offset
+// `voff` + `soff` of the buffer to LDS address m0 + 16 * lane, zeros where
+// the access lies past the descriptor's range. Issued from asm for the same
+// reason as lds_dma16.
+__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, unsigned int voff, unsigned int soff,
+                                              unsigned int lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+
+// Per-lane constants of the tile loads from one strided bf16 matrix. Wave w
+// (of 4) loads tile rows 16w .. 16w + 15 with two instructions, each writing
+// 8 whole rows (1 KB) at lane-contiguous LDS addresses: lane l moves chunk
+// (l & 7) ^ swz(row) of row 16w + 8i + l/8. The byte offsets need
+// 64 * row_stride * 2 < 2^32 (the host checks the channel count).
+struct TileLoader {
+    unsigned int voff[2];  // byte offset of the lane's chunk from the tile's first row
+    unsigned int lds[2];   // byte offset of the instruction's rows within a tile
+};
+
+__device__ __forceinline__ TileLoader tile_loader(long long row_stride, int wave, int lane) {
+    TileLoader L;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tr = 16 * wave + 8 * i + (lane >> 3);
-        const int c = (lane & 7) ^ swz(tr);
-        const int row = min(r0 + tr, nrows - 1);
-        const bf16* g = base + (long long)row * row_stride + c * 8;
-        const unsigned int dst = __builtin_amdgcn_readfirstlane(lds_addr(tile + (16 * wave + 8 * i) * 64));
-        lds_dma16(g, dst);
+        const int col = ((lane & 7) ^ swz(tr)) * 8;
+        L.voff[i] = (unsigned int)(((long long)tr * row_stride + col) * 2);
+        L.lds[i] = __builtin_amdgcn_readfirstlane((unsigned int)(16 * wave + 8 * i) * 128u);
     }
+    return L;
+}
+
+// Descriptor over rows [r0, nrows) of a strided bf16 matrix (row stride
+// `row_stride` elements, nrows > r0): loads of rows past the matrix return
+// zeros (callers mask or zero-weight them).
+__device__ __forceinline__ i32x4 rows_rsrc(const bf16* base, long long row_stride, int r0,
+                                           int nrows) {
+    const unsigned long long bytes = (unsigned long long)(nrows - r0) * row_stride * 2;
+    return buffer_rsrc(base + (long long)r0 * row_stride,
+                       bytes > 0xffffffffull ? 0xffffffffu : (unsigned int)bytes);
+}
+
+// Issue the loads of the 64 rows of a descriptor from rows_rsrc into the LDS
+// tile at byte address `lds_tile`; `soff` (bytes) selects columns further
+// along the same rows (V next to K in the packed qkv rows). A row is in range
+// when its offset without `soff` is, and also with it, since soff + 128
+// bytes stays within one row.
+__device__ __forceinline__ void atile_load(unsigned int lds_tile, i32x4 rsrc, unsigned int soff,
+                                           const TileLoader& L) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16_buf(rsrc, L.voff[i], soff, lds_tile + L.lds[i]);
+}
+
+// Wave-uniform LDS byte address of a tile.
+__device__ __forceinline__ unsigned int atile_addr(const bf16* tile) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(tile));
 }
 
 // LDS address of a tile as seen by its readers. The direct loads above write

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ qkv, bf16* __restrict__ out, float* __restrict__ lse,
     int B, int T, int H, int n_qt, float c_log2) {
     __shared__ FwdSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
 
     // Workgroup -> (query tile, head): heaviest (last) query tiles first;
@@ -66,9 +67,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
     const int b = bh / H, h = bh - b * H;
     const int C = H * HEAD_DIM;
     const long long rs = 3LL * C;  // qkv token stride, elements
+    const TileLoader ld_rs = tile_loader(rs, wave, lane);
     const bf16* qbase = qkv + (long long)b * T * rs + h * HEAD_DIM;
     const bf16* kbase = qbase + C;
-    const bf16* vbase = qbase + 2 * C;
 
     const int q0 = qt * FWD_BM;
     const int qw = q0 + wave * 32 * FWD_QB;  // first query of this wave
@@ -93,12 +94,16 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
         acc[qb][0] = acc[qb][1] = zero16();
     }
 
+    // K and V rows [k0, k0 + 64) into stage st: one descriptor, since V sits
+    // C elements after K in every packed row.
+    auto issue = [&](int k0, int st) {
+        const i32x4 kv = rows_rsrc(kbase, rs, k0, T);
+        atile_load(atile_addr(sm.k[st]), kv, 0, ld_rs);
+        atile_load(atile_addr(sm.v[st]), kv, 2u * C, ld_rs);
+    };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < n_kt) {
-            atile_load(sm.k[j], kbase, rs, j * FWD_BN, T, wave, lane);
-            atile_load(sm.v[j], vbase, rs, j * FWD_BN, T, wave, lane);
-        }
+        if (j < n_kt) issue(j * FWD_BN, j);
 
     // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of each block's query.
     bf16x8 qreg[FWD_QB][4];
@@ -118,11 +123,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
         if (j + 1 < n_kt) wait_vmem<LOADS_PER_TILE>();
         else wait_vmem<0>();
         __syncthreads();
-        if (j + NSTAGE - 1 < n_kt) {
-            const int st = (j + NSTAGE - 1) % NSTAGE;
-            atile_load(sm.k[st], kbase, rs, (j + NSTAGE - 1) * FWD_BN, T, wave, lane);
-            atile_load(sm.v[st], vbase, rs, (j + NSTAGE - 1) * FWD_BN, T, wave, lane);
-        }
+        if (j + NSTAGE - 1 < n_kt) issue((j + NSTAGE - 1) * FWD_BN, (j + NSTAGE - 1) % NSTAGE);
         const int k0 = j * FWD_BN;
         if (k0 > qw + 32 * FWD_QB - 1) continue;  // whole tile above this wave's diagonal
         const int st = j % NSTAGE;

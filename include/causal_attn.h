@@ -52,8 +52,8 @@
  * streams may run concurrently as long as their buffers do not overlap.
  *
  * Shapes: head_dim must be 64. B, T and n_head may be any non-negative value
- * whose tensors fit in 2^62 bytes and whose launch grids fit in 2^31 - 1
- * workgroups; a call with B, T or n_head equal to 0 has nothing to compute
+ * with n_head * head_dim <= 2^23, whose tensors fit in 2^62 bytes and whose
+ * launch grids fit in 2^31 - 1 workgroups; a call with B, T or n_head equal to 0 has nothing to compute
  * and returns ATTN_OK without touching memory (its pointers may then be
  * NULL). qkv, out, dout, dqkv and delta must start on a 16-byte boundary,
  * lse on a 4-byte boundary. Outputs may not overlap inputs or each other.

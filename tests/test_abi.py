@@ -81,6 +81,7 @@ def test_forward_validation(L, fn):
     assert f(Q, O, LS, 1, 64, 2, 32, None) == -3
     assert f(Q, O, LS, 2**31 - 1, 2**31 - 1, 2**20, 64, None) == -4
     assert f(Q, O, LS, 1, 2**31 - 1, 2**20, 64, None) == -4
+    assert f(Q, O, LS, 1, 64, 2**17 + 1, 64, None) == -4   # n_head*head_dim > 2^23
     assert f(Q + 8, O, LS, *ok, None) == -5
     assert f(Q, O + 4, LS, *ok, None) == -5
     assert f(Q, O, LS + 2, *ok, None) == -5
