@@ -163,10 +163,6 @@ __device__ __forceinline__ void dkdv_acc(lds_bf16* qt, lds_bf16* gt, const int (
     }
 }
 
-#ifndef CATTN_DKDV_SCHED
-#define CATTN_DKDV_SCHED 0
-#endif
-
 template <bool MASK>
 __device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
                                           __attribute__((address_space(3))) const float* stats,
@@ -182,15 +178,6 @@ __device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
     dkdv_acc<0>(qt, gt, troff, pds0, dvt, dkt);
     dkdv_pds<1, MASK>(stats, s1, dp1, lim, c_log2, hf, pds1);
     dkdv_acc<1>(qt, gt, troff, pds1, dvt, dkt);
-#if CATTN_DKDV_SCHED == 1
-    __builtin_amdgcn_iglp_opt(0);
-#elif CATTN_DKDV_SCHED == 2
-    __builtin_amdgcn_iglp_opt(1);
-#elif CATTN_DKDV_SCHED == 3
-    __builtin_amdgcn_iglp_opt(2);
-#elif CATTN_DKDV_SCHED == 4
-    __builtin_amdgcn_iglp_opt(3);
-#endif
 }
 
 __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_bf16_kernel(

@@ -6,15 +6,20 @@
 // the theprofessional.online summary, row "flash attention"), written for
 // CDNA4 from the definition rather than from any published kernel.
 //
-// One workgroup = 4 waves = 4 * 32 * QB queries of one (batch, head); wave w
-// owns QB blocks of 32 queries. Key/value tiles of 64 rows stream through a
-// three-stage ring of LDS buffers filled by direct global->LDS loads, so two
-// tiles are in flight while a third is consumed. Per tile, a wave computes
-// S^T = K Q^T on MFMA (lane l%32 owns query l%32, so row statistics live in
-// one lane pair), masks only the tile on its diagonal, and accumulates
-// O^T += V^T P^T on MFMA with P^T fed straight from registers and V^T read
-// from the row-major V tile by transposing LDS reads. Each LDS operand read
-// feeds all QB query blocks. Tiles above a wave's diagonal are skipped.
+// One workgroup = 4 waves = 128 queries of one (batch, head); wave w owns
+// queries q0 + 32w .. +31. Key/value tiles of 64 rows stream through a
+// three-stage ring of LDS buffers filled by direct buffer->LDS loads. Per
+// tile, a wave computes S^T = K Q^T on MFMA (lane l%32 owns query l%32, so
+// row statistics live in one lane pair), masks only its last tile (the one
+// holding its diagonal), and accumulates O^T += V^T P^T on MFMA with P^T fed
+// straight from registers and V^T read from the row-major V tile by
+// transposing LDS reads. Tiles above a wave's diagonal are skipped.
+//
+// The tile loop is software-pipelined across tiles: while the exponentials
+// of tile j run on the VALU, the MFMAs of S for tile j+1 are in flight, and
+// while P V of tile j runs on MFMA, the VALU sums tile j's row and takes the
+// row max of tile j+1. So each wave keeps the matrix cores and the vector
+// ALU busy at once, instead of alternating between them.
 //
 // Softmax in base 2 with a lazily updated running max: the accumulator is
 // rescaled only when some row's tile max exceeds its running max by more
@@ -23,18 +28,16 @@
 // function: O = acc / l and LSE = ln 2 * (m + log2 l) for whichever m was used.
 #include "attn_common.h"
 
-#ifndef CATTN_FWD_QB
-#define CATTN_FWD_QB 1
+#ifndef CATTN_FWD_WAVES_PER_SIMD
+#define CATTN_FWD_WAVES_PER_SIMD 1
 #endif
 
 namespace cattn {
 namespace {
 
-constexpr int FWD_QB = CATTN_FWD_QB;  // 32-query blocks per wave
-constexpr int FWD_BM = 128 * FWD_QB;  // queries per workgroup
-constexpr int FWD_BN = 64;            // keys per tile
-constexpr int NSTAGE = 3;
-constexpr int LOADS_PER_TILE = 4;     // per wave: 2 for K, 2 for V
+constexpr int FWD_BM = 128;  // queries per workgroup (32 per wave)
+constexpr int FWD_BN = 64;   // keys per tile
+constexpr int NSTAGE = 3;    // tile j (V), tile j+1 (K) in use, tile j+2 in flight
 constexpr float RESCALE_LOG2 = 8.0f;
 
 struct FwdSmem {
@@ -42,7 +45,100 @@ struct FwdSmem {
     bf16 v[NSTAGE][ATILE_ELEMS];  // V tiles, row-major [key][d] (swizzled)
 };
 
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// S^T = K Q^T for one 64-key tile: two 32-key blocks of 4 MFMAs each.
+__device__ __forceinline__ void scores(lds_bf16* kt, const int (&koff)[4],
+                                       const bf16x8 (&qreg)[4], f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            s[kb] = mfma32(*reinterpret_cast<lds_bf16x8*>(kt + kb * 32 * 64 + koff[kk]), qreg[kk],
+                           s[kb]);
+    }
+}
+
+// Causal mask of a wave's last tile: key k0 + kb*32 + 8(i/4) + 4hf + (i%4)
+// against query qw + l32; `lim` = qw - k0 + l32 - 4hf.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
+}
+
+// Row max of a tile (both lane halves), times c = scale * log2 e.
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c_log2) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    return fmaxf(mx, swap_halves(mx)) * c_log2;
+}
+
+// Take the new tile max into the running max: a row rescales (acc, l) only
+// when its tile max exceeds the running max by more than 2^8. Each row
+// decides for itself (rows that keep their max scale by exactly 1), so a
+// row's arithmetic never depends on the other rows of the wave and later
+// tokens cannot change earlier rows.
+__device__ __forceinline__ void update_max(float mt, float& m_run, float& l_run,
+                                           f32x16 (&acc)[2]) {
+    const bool grow = mt > m_run + RESCALE_LOG2;
+    if (__any(grow)) {
+        asm volatile("");  // keeps the branch: rescales are rare after the first tiles
+        const float m_new = grow ? mt : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+}
+
+enum NextTile { NEXT_NONE, NEXT_PLAIN, NEXT_MASKED };
+
+// One pipelined tile step: P = exp2(c s - m) of tile j (in place in `s`)
+// with the scores of tile j+1 (into `s_next`) on MFMA, then O^T += V^T P^T
+// of tile j with the row sum of tile j and the mask and row max of tile j+1
+// on the VALU. The caller swaps the roles of the two score buffers.
+template <int NEXT>
+__device__ __forceinline__ void tile_step(f32x16 (&s)[2], f32x16 (&s_next)[2], lds_bf16* kt_next,
+                                          lds_bf16* vt, const int (&koff)[4],
+                                          const int (&voff)[2][2], const bf16x8 (&qreg)[4],
+                                          f32x16 (&acc)[2], float& m_run, float& l_run,
+                                          float c_log2, int lim_next) {
+    if (NEXT != NEXT_NONE) scores(kt_next, koff, qreg, s_next);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m_run));
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) pb[kc] = c_rows_to_operand(s[kc >> 1], kc & 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            acc[db] = mfma32(atile_tr(vt, voff[db][0], voff[db][1], kc), pb[kc], acc[db]);
+    float rsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rsum += s[kb][i];
+    l_run += rsum;
+    if (NEXT != NEXT_NONE) {
+        if (NEXT == NEXT_MASKED) mask_tile(s_next, lim_next);
+        update_max(tile_max(s_next, c_log2), m_run, l_run, acc);
+    }
+}
+
+__global__ __launch_bounds__(256, CATTN_FWD_WAVES_PER_SIMD) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ qkv, bf16* __restrict__ out, float* __restrict__ lse,
     int B, int T, int H, int n_qt, float c_log2) {
     __shared__ FwdSmem sm;
@@ -72,10 +168,14 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
     const bf16* kbase = qbase + C;
 
     const int q0 = qt * FWD_BM;
-    const int qw = q0 + wave * 32 * FWD_QB;  // first query of this wave
+    const int qw = q0 + wave * 32;  // first query of this wave
 
     const int kend = min(q0 + FWD_BM, T);
     const int n_kt = (kend + FWD_BN - 1) / FWD_BN;
+    // This wave's last tile: the one holding key qw + 31 (its diagonal), or
+    // the workgroup's last tile when the sequence ends first. Only this tile
+    // can hold keys above one of the wave's queries.
+    const int j_last = min((qw + 31) / FWD_BN, n_kt - 1);
 
     // Per-lane LDS offsets: K rows kb*32 + l32 at chunks 2kk + hf; V^T reads.
     int koff[4];
@@ -85,15 +185,6 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &voff[db][0], &voff[db][1]);
 
-    float m_run[FWD_QB], l_run[FWD_QB];
-    f32x16 acc[FWD_QB][2];  // O^T per (query block, d block)
-#pragma unroll
-    for (int qb = 0; qb < FWD_QB; ++qb) {
-        m_run[qb] = -INFINITY;  // running max of c*s
-        l_run[qb] = 0.0f;       // this lane half's share of the row sum
-        acc[qb][0] = acc[qb][1] = zero16();
-    }
-
     // K and V rows [k0, k0 + 64) into stage st: one descriptor, since V sits
     // C elements after K in every packed row.
     auto issue = [&](int k0, int st) {
@@ -101,139 +192,73 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(
         atile_load(atile_addr(sm.k[st]), kv, 0, ld_rs);
         atile_load(atile_addr(sm.v[st]), kv, 2u * C, ld_rs);
     };
-#pragma unroll
-    for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < n_kt) issue(j * FWD_BN, j);
+    issue(0, 0);
+    if (n_kt > 1) issue(FWD_BN, 1);
 
-    // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of each block's query.
-    bf16x8 qreg[FWD_QB][4];
-#pragma unroll
-    for (int qb = 0; qb < FWD_QB; ++qb) {
-        const int q = qw + 32 * qb + l32;
+    // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of this lane's query.
+    bf16x8 qreg[4];
+    {
+        const int q = qw + l32;
         const bf16* p = qbase + (long long)q * rs + hf * 8;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qreg[qb][kk] = as_bf16x8(load16(p + kk * 16, q < T));
+        for (int kk = 0; kk < 4; ++kk) qreg[kk] = as_bf16x8(load16(p + kk * 16, q < T));
     }
-    // Everything issued so far (the first tiles and Q) lands before the loop,
-    // so the compiler needs no waits on Q inside it.
+    // Tiles 0 and 1 and Q land before the loop (no waits on Q inside it).
     wait_vmem<0>();
+    __syncthreads();
 
-    for (int j = 0; j < n_kt; ++j) {
-        // Tile j has landed once at most the next tile's loads are pending.
-        if (j + 1 < n_kt) wait_vmem<LOADS_PER_TILE>();
-        else wait_vmem<0>();
+    float m_run = -INFINITY;  // running max of c*s
+    float l_run = 0.0f;       // this lane half's share of the row sum
+    f32x16 acc[2] = {zero16(), zero16()};  // O^T per d block
+    f32x16 s[2], s_next[2];
+    {
+        scores(atile_view(sm.k[0]), koff, qreg, s);
+        if (j_last == 0) mask_tile(s, qw + l32 - 4 * hf);
+        update_max(tile_max(s, c_log2), m_run, l_run, acc);
+    }
+
+    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        // Tile j+1 (issued one step ago) has landed everywhere, and every wave
+        // has left step j-1, so its stage can take tile j+2.
+        wait_vmem<0>();
         __syncthreads();
-        if (j + NSTAGE - 1 < n_kt) issue((j + NSTAGE - 1) * FWD_BN, (j + NSTAGE - 1) % NSTAGE);
-        const int k0 = j * FWD_BN;
-        if (k0 > qw + 32 * FWD_QB - 1) continue;  // whole tile above this wave's diagonal
-        const int st = j % NSTAGE;
-        lds_bf16* kt = atile_view(sm.k[st]);
-        lds_bf16* vt = atile_view(sm.v[st]);
-
-        // S^T = K Q^T for every query block; each K operand read feeds QB MFMAs.
-        f32x16 s[FWD_QB][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int qb = 0; qb < FWD_QB; ++qb) s[qb][kb] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-                const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(kt + kb * 32 * 64 + koff[kk]);
-#pragma unroll
-                for (int qb = 0; qb < FWD_QB; ++qb) s[qb][kb] = mfma32(a, qreg[qb][kk], s[qb][kb]);
-            }
-        }
-        // Causal mask on the tile that holds a block's diagonal: key > query -> -inf.
-#pragma unroll
-        for (int qb = 0; qb < FWD_QB; ++qb) {
-            const int qblk = qw + 32 * qb;
-            if (k0 + FWD_BN - 1 > qblk) {
-                const int lim = qblk - k0 + l32 - 4 * hf;  // key - k0 must be <= this
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[qb][kb][i] = -INFINITY;
-            }
-        }
-        float mt[FWD_QB];
-        bool grow[FWD_QB], any_grow = false;
-#pragma unroll
-        for (int qb = 0; qb < FWD_QB; ++qb) {
-            float mx = s[qb][0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-            mx = fmaxf(mx, swap_halves(mx));
-            mt[qb] = mx * c_log2;
-            grow[qb] = mt[qb] > m_run[qb] + RESCALE_LOG2;
-            any_grow |= grow[qb];
-        }
-        // Each row decides for itself (rows that do not grow keep their max
-        // and scale by exactly 1), so a row's arithmetic never depends on the
-        // other rows of the wave: later tokens cannot change earlier rows.
-        if (__any(any_grow)) {
-#pragma unroll
-            for (int qb = 0; qb < FWD_QB; ++qb) {
-                const float m_new = grow[qb] ? mt[qb] : m_run[qb];
-                const float alpha = grow[qb] ? fast_exp2(m_run[qb] - m_new) : 1.0f;
-                l_run[qb] *= alpha;
-                m_run[qb] = m_new;
-#pragma unroll
-                for (int db = 0; db < 2; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
-            }
-        }
-        bf16x8 pb[FWD_QB][4];
-#pragma unroll
-        for (int qb = 0; qb < FWD_QB; ++qb) {
-            float rsum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(fmaf(s[qb][kb][i], c_log2, -m_run[qb]));
-                    s[qb][kb][i] = p;
-                    rsum += p;
-                }
-            l_run[qb] += rsum;
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) pb[qb][kc] = c_rows_to_operand(s[qb][kc >> 1], kc & 1);
-        }
-        // O^T += V^T P^T over four 16-key chunks; each V^T operand feeds QB MFMAs.
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const bf16x8 a = atile_tr(vt, voff[db][0], voff[db][1], kc);
-#pragma unroll
-                for (int qb = 0; qb < FWD_QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][kc], acc[qb][db]);
-            }
+        if (j + 2 < n_kt) issue((j + 2) * FWD_BN, (j + 2) % NSTAGE);
+        if (j > j_last) return;  // tiles above this wave's diagonal
+        lds_bf16* vt = atile_view(sm.v[j % NSTAGE]);
+        lds_bf16* kt_next = atile_view(sm.k[(j + 1) % NSTAGE]);
+        const int lim_next = qw - (j + 1) * FWD_BN + l32 - 4 * hf;
+        if (j + 1 < j_last)
+            tile_step<NEXT_PLAIN>(cur, nxt, kt_next, vt, koff, voff, qreg, acc, m_run, l_run,
+                                  c_log2, lim_next);
+        else if (j + 1 == j_last)
+            tile_step<NEXT_MASKED>(cur, nxt, kt_next, vt, koff, voff, qreg, acc, m_run, l_run,
+                                   c_log2, lim_next);
+        else
+            tile_step<NEXT_NONE>(cur, nxt, kt_next, vt, koff, voff, qreg, acc, m_run, l_run,
+                                 c_log2, lim_next);
+    };
+    // Two steps per trip, so the two score buffers trade roles without copies.
+    for (int j = 0; j < n_kt; j += 2) {
+        step(j, s, s_next);
+        if (j + 1 < n_kt) step(j + 1, s_next, s);
     }
 
     // Epilogue: O = acc / l (rounded to bf16), LSE = ln 2 * (m + log2 l).
+    const int q = qw + l32;
+    const float l_tot = l_run + swap_halves(l_run);
+    const float inv = 1.0f / l_tot;
+    if (q < T) {
+        bf16* op = out + ((long long)b * T + q) * C + h * HEAD_DIM;
 #pragma unroll
-    for (int qb = 0; qb < FWD_QB; ++qb) {
-        const int q = qw + 32 * qb + l32;
-        const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
-        const float inv = 1.0f / l_tot;
-        if (q < T) {
-            bf16* op = out + ((long long)b * T + q) * C + h * HEAD_DIM;
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d = db * 32 + 8 * g + 4 * hf;
-                    const f32x16& a = acc[qb][db];
-                    *reinterpret_cast<u32x2*>(op + d) =
-                        to_bf16x4_bits(a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv,
-                                       a[4 * g + 3] * inv);
-                }
-            if (hf == 0) lse[(long long)bh * T + q] = (m_run[qb] + log2f(l_tot)) * LN2;
-        }
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + 8 * g + 4 * hf;
+                *reinterpret_cast<u32x2*>(op + d) =
+                    to_bf16x4_bits(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                                   acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+            }
+        if (hf == 0) lse[(long long)bh * T + q] = (m_run + log2f(l_tot)) * LN2;
     }
 }
 
