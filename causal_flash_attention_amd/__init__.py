@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
+    attn_bwd_dq_preprocess,
     attn_bwd_preprocess,
     attn_fwd,
     attn_last_error,

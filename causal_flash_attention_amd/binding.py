@@ -36,6 +36,7 @@ SIGNATURES = {
     "attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_preprocess": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_dq_preprocess": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_dkdv": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_dq": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
@@ -161,6 +162,18 @@ def _require_ws(delta, B, T, n_head):
 
 def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
              stream=None) -> None:
+    _bwd_full("attn_bwd", dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
+
+
+def attn_bwd_dq_preprocess(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
+                           stream=None) -> None:
+    if qkv is not None and qkv.dtype != _torch().bfloat16:
+        raise ValueError("attn_bwd_dq_preprocess takes bfloat16 tensors")
+    _bwd_full("attn_bwd_dq_preprocess", dout, qkv, out, lse, dqkv, delta, n_head, head_dim,
+              stream)
+
+
+def _bwd_full(name, dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream) -> None:
     torch = _torch()
     dt, sfx = _elem(qkv)
     B, T, C = _dims(qkv, n_head, head_dim)
@@ -170,9 +183,9 @@ def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
     _require(lse, "lse", torch.float32, (B, n_head, T))
     _require(dqkv, "dqkv", dt, (B, T, 3 * C))
     _require_ws(delta, B, T, n_head)
-    fn = getattr(lib(), "attn_bwd" + sfx)
+    fn = getattr(lib(), name + sfx)
     _check(fn(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dqkv), _ptr(delta),
-              B, T, n_head, head_dim, _stream_ptr(stream)), "attn_bwd" + sfx)
+              B, T, n_head, head_dim, _stream_ptr(stream)), name + sfx)
 
 
 def attn_bwd_preprocess(dout, out, lse, delta, n_head: int, head_dim: int = 64,

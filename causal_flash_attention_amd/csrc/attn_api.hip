@@ -14,6 +14,8 @@ hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, voi
                                      hipStream_t);
 hipError_t launch_attn_bwd_dq_bf16(const void*, const void*, const float*, void*, int, int, int,
                                    hipStream_t);
+hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
+                                       void*, int, int, int, hipStream_t);
 hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
 hipError_t launch_attn_bwd_pre_f32(const float*, const float*, const float*, float*, int, int, int,
                                    hipStream_t);
@@ -187,7 +189,16 @@ int bwd_common(const void* dout, const void* qkv, const void* out, const float* 
 
     const hipStream_t s = as_stream(stream);
     hipError_t e = hipSuccess;
-    if (elem == 2) {
+    if (elem == 2 && (stages & kPre) && (stages & kDq)) {
+        // The dQ kernel computes the workspace for its own rows on the way
+        // (same values as the preprocess stage); dK/dV then reads it.
+        e = cattn::launch_attn_bwd_dq_pre_bf16(qkv, dout, out, lse, ws, dqkv, B, T, H, s);
+        if (e != hipSuccess) return fail_hip(e, "attn_bwd dQ launch");
+        if (stages & kDkdv) {
+            e = cattn::launch_attn_bwd_dkdv_bf16(qkv, dout, ws, dqkv, B, T, H, s);
+            if (e != hipSuccess) return fail_hip(e, "attn_bwd dK/dV launch");
+        }
+    } else if (elem == 2) {
         if (stages & kPre) {
             e = cattn::launch_attn_bwd_pre_bf16(dout, out, lse, ws, B, T, H, s);
             if (e != hipSuccess) return fail_hip(e, "attn_bwd preprocess launch");
@@ -239,6 +250,13 @@ int attn_bwd_preprocess(const void* dout, const void* out, const float* lse, flo
                         int T, int n_head, int head_dim, void* stream) {
     return bwd_common(dout, nullptr, out, lse, nullptr, delta, B, T, n_head, head_dim, stream, 2,
                       kPre);
+}
+
+int attn_bwd_dq_preprocess(const void* dout, const void* qkv, const void* out, const float* lse,
+                           void* dqkv, float* delta, int B, int T, int n_head, int head_dim,
+                           void* stream) {
+    return bwd_common(dout, qkv, out, lse, dqkv, delta, B, T, n_head, head_dim, stream, 2,
+                      kPre | kDq);
 }
 
 int attn_bwd_dkdv(const void* dout, const void* qkv, const float* delta, void* dqkv, int B, int T,

@@ -33,10 +33,26 @@ constexpr int ROW_PAD = 64;
 constexpr int NSTAGE = 3;
 
 // ---------------------------------------------------------------------------
-// Preprocess. Blocks [0, nb_d): D[b, h, t] = sum_k dO[b,t,h,k] O[b,t,h,k], 8
-// lanes per (b, t, h). Blocks [nb_d, ...): one thread per padded (bh, t):
-// LSE * log2 e, and the padding of both arrays.
+// Preprocess: D[b, h, t] = sum_k dO[b,t,h,k] O[b,t,h,k] and LSE * log2 e, with
+// the padding of both. The dQ kernel can do the same work for its own rows
+// (the fused form used by attn_bwd); both compute D in one fixed order, so
+// the staged and fused workspaces agree bit for bit.
 // ---------------------------------------------------------------------------
+
+// Half of D: the 32 products of k = 16kk + 8*half + e, kk and e ascending,
+// in one fmaf chain from zero. D = (half 0) + (half 1).
+__device__ __forceinline__ float dot_half(const bf16x8 (&g)[4], const bf16x8 (&o)[4]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)g[kk][e], (float)o[kk][e], acc);
+    return acc;
+}
+
+// Blocks [0, nb_d): D, two lanes per (b, t, h) row (one per half).
+// Blocks [nb_d, ...): one thread per padded (bh, t): LSE * log2 e, and the
+// padding of both arrays.
 __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
     const bf16* __restrict__ dout, const bf16* __restrict__ out, const float* __restrict__ lse,
     float* __restrict__ ws, int T, int Tp, int H, long long n_rows, long long nb_d,
@@ -45,20 +61,21 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
     float* __restrict__ dd = ws;
     float* __restrict__ lse2 = ws + n_pad_rows;
     if (blk < nb_d) {
-        const long long row = blk * 32 + (threadIdx.x >> 3);
-        const int part = threadIdx.x & 7;
+        const long long row = blk * 128 + (threadIdx.x >> 1);
+        const int half = threadIdx.x & 1;
         float acc = 0.0f;
         if (row < n_rows) {
-            const long long off = row * HEAD_DIM + part * 8;  // rows are (b, t, h) in memory order
-            const bf16x8 g = as_bf16x8(*reinterpret_cast<const u32x4*>(dout + off));
-            const bf16x8 o = as_bf16x8(*reinterpret_cast<const u32x4*>(out + off));
+            const long long off = row * HEAD_DIM + half * 8;  // rows are (b, t, h) in memory order
+            bf16x8 g[4], o[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf((float)g[e], (float)o[e], acc);
+            for (int kk = 0; kk < 4; ++kk) {
+                g[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(dout + off + 16 * kk));
+                o[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(out + off + 16 * kk));
+            }
+            acc = dot_half(g, o);
         }
         acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        acc += __shfl_xor(acc, 4, 64);
-        if (row < n_rows && part == 0) {
+        if (row < n_rows && half == 0) {
             const long long bt = row / H;
             const int h = (int)(row - bt * H);
             const long long b = bt / T;
@@ -371,9 +388,14 @@ __device__ __forceinline__ void dq_tile(lds_bf16* kt, lds_bf16* vt, const bf16x8
     dq_half<1, MASK>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
 }
 
+// FUSED_PRE: also compute D and LSE * log2 e of this workgroup's rows from
+// dout, out and lse (instead of reading them from the workspace) and write
+// them, with the padding, to the workspace for the dK/dV kernel.
+template <bool FUSED_PRE>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
-    bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_qt, float c_log2, float scale) {
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const bf16* __restrict__ out,
+    const float* __restrict__ lse, float* __restrict__ ws, bf16* __restrict__ dqkv, int B, int T,
+    int Tp, int H, int n_qt, float c_log2, float scale) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
@@ -436,9 +458,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
             greg[kk] = as_bf16x8(load16(gp + kk * 16, q_ok));
         }
     }
-    const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
-    const float dd = q_ok ? ws[ws_i] : 0.0f;
-    const float lse2 = q_ok ? ws[(long long)BH * Tp + ws_i] : INFINITY;
+    float dd, lse2;
+    if (FUSED_PRE) {
+        bf16x8 oreg[4];
+        const bf16* op = out + ((long long)b * T + my_q) * C + h * HEAD_DIM + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) oreg[kk] = as_bf16x8(load16(op + kk * 16, q_ok));
+        const float part = dot_half(greg, oreg);  // zero past T
+        dd = part + swap_halves(part);
+        lse2 = q_ok ? lse[(long long)bh * T + my_q] * LOG2E : INFINITY;
+        if (hf == 0 && my_q < Tp) {
+            ws[(long long)bh * Tp + my_q] = dd;
+            ws[(long long)BH * Tp + (long long)bh * Tp + my_q] = lse2;
+        }
+    } else {
+        const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
+        dd = q_ok ? ws[ws_i] : 0.0f;
+        lse2 = q_ok ? ws[(long long)BH * Tp + ws_i] : INFINITY;
+    }
     // The first tiles and this lane's Q, dO, LSE, D land before the loop.
     wait_vmem<0>();
 
@@ -482,7 +519,7 @@ hipError_t launch_attn_bwd_pre_bf16(const void* dout, const void* out, const flo
                                     int B, int T, int H, hipStream_t stream) {
     const int Tp = bwd_padded_rows(T);
     const long long n_rows = (long long)B * T * H;
-    const long long nb_d = (n_rows + 31) / 32;
+    const long long nb_d = (n_rows + 127) / 128;
     const long long n_pad_rows = (long long)B * H * Tp;
     const long long nb_l = (n_pad_rows + 255) / 256;
     hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)(nb_d + nb_l)), dim3(256), 0,
@@ -506,10 +543,22 @@ hipError_t launch_attn_bwd_dq_bf16(const void* qkv, const void* dout, const floa
                                    int B, int T, int H, hipStream_t stream) {
     const int n_qt = (T + DQ_BM - 1) / DQ_BM;
     const long long blocks = (long long)B * H * n_qt;
-    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), ws,
-                       static_cast<bf16*>(dqkv), B, T, bwd_padded_rows(T), H, n_qt,
-                       LOG2E / 8.0f, 0.125f);
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), nullptr,
+                       nullptr, const_cast<float*>(ws), static_cast<bf16*>(dqkv), B, T,
+                       bwd_padded_rows(T), H, n_qt, LOG2E / 8.0f, 0.125f);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq_pre_bf16(const void* qkv, const void* dout, const void* out,
+                                       const float* lse, float* ws, void* dqkv, int B, int T,
+                                       int H, hipStream_t stream) {
+    const int n_qt = (T + DQ_BM - 1) / DQ_BM;
+    const long long blocks = (long long)B * H * n_qt;
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout),
+                       static_cast<const bf16*>(out), lse, ws, static_cast<bf16*>(dqkv), B, T,
+                       bwd_padded_rows(T), H, n_qt, LOG2E / 8.0f, 0.125f);
     return hipGetLastError();
 }
 

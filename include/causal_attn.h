@@ -88,21 +88,30 @@ int attn_fwd(const void* qkv, void* out, float* lse,
 
 /* Backward: dqkv = gradients of sum(dout * out) with respect to qkv, given
  * the out and lse written by attn_fwd for the same qkv. Runs
- * attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq in that order on
- * `stream`; `delta` is the caller's workspace (layout above). */
+ * attn_bwd_dq_preprocess and then attn_bwd_dkdv on `stream` (two kernels);
+ * `delta` is the caller's workspace (layout above). */
 int attn_bwd(const void* dout, const void* qkv, const void* out, const float* lse,
              void* dqkv, float* delta,
              int B, int T, int n_head, int head_dim, void* stream);
 
-/* The three stages of attn_bwd, exported so that each kernel can be launched
- * and timed on its own.
- *   attn_bwd_preprocess: D = rowsum(dout * out) and LSE * log2(e) into delta
- *   attn_bwd_dkdv:       writes the dK and dV blocks of dqkv
- *   attn_bwd_dq:         writes the dQ block of dqkv
- * dkdv and dq read delta, so they must follow preprocess on the stream;
- * they write disjoint columns of dqkv and may run in either order. */
+/* The stages of attn_bwd, exported so that each kernel can be launched and
+ * timed on its own.
+ *   attn_bwd_preprocess:    D = rowsum(dout * out) and LSE * log2(e) into delta
+ *   attn_bwd_dkdv:          writes the dK and dV blocks of dqkv (reads delta)
+ *   attn_bwd_dq:            writes the dQ block of dqkv (reads delta)
+ *   attn_bwd_dq_preprocess: one kernel doing the work of attn_bwd_preprocess
+ *                           and attn_bwd_dq (each row's D and LSE * log2(e)
+ *                           are computed where its dQ is, and written to
+ *                           delta); same arguments as attn_bwd
+ * attn_bwd is attn_bwd_dq_preprocess followed by attn_bwd_dkdv. The staged
+ * sequence preprocess, dkdv, dq gives the same dqkv and delta bit for bit.
+ * dkdv and dq must follow the stage that writes delta on the stream; they
+ * write disjoint columns of dqkv and may run in either order. */
 int attn_bwd_preprocess(const void* dout, const void* out, const float* lse, float* delta,
                         int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_dq_preprocess(const void* dout, const void* qkv, const void* out,
+                           const float* lse, void* dqkv, float* delta,
+                           int B, int T, int n_head, int head_dim, void* stream);
 int attn_bwd_dkdv(const void* dout, const void* qkv, const float* delta, void* dqkv,
                   int B, int T, int n_head, int head_dim, void* stream);
 int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqkv,

@@ -43,7 +43,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
-              "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_workspace_floats",
+              "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess", "attn_bwd_workspace_floats",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -121,6 +121,10 @@ def test_stage_validation(L):
     assert L.attn_bwd_dkdv(G, Q, DL, DQ, 1, 64, 2, 16, None) == -3
     assert L.attn_bwd_dq(G, Q, DL, Q, *ok, None) == -6
     assert L.attn_bwd_dq(G, Q, DQ + 32, DQ, *ok, None) == -6  # workspace read inside dqkv
+    assert L.attn_bwd_dq_preprocess(G, Q, O, LS, DQ, None, *ok, None) == -1
+    assert L.attn_bwd_dq_preprocess(G, Q, None, LS, DQ, DL, *ok, None) == -1   # needs out
+    assert L.attn_bwd_dq_preprocess(G, Q, O, LS, DQ, DQ + 64, *ok, None) == -6  # delta in dqkv
+    assert L.attn_bwd_dq_preprocess(G, Q, O, LS, DQ, DL + 4, *ok, None) == -5
 
 
 def test_workspace_size(L):
@@ -140,6 +144,7 @@ def test_empty_problems_are_noops(L):
         assert L.attn_bwd_f32(None, None, None, None, None, None, B, T, H, 64, None) == 0
         assert L.attn_bwd_dkdv(None, None, None, None, B, T, H, 64, None) == 0
         assert L.attn_bwd_preprocess(None, None, None, None, B, T, H, 64, None) == 0
+        assert L.attn_bwd_dq_preprocess(None, None, None, None, None, None, B, T, H, 64, None) == 0
 
 
 @no_gpu_only

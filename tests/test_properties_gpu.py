@@ -75,14 +75,26 @@ def test_stage_entry_points_match_attn_bwd():
     qkv, dout = _inputs(B, T, H, "bf16", seed=41)
     qd, gd = to_device(qkv, "bf16"), to_device(dout, "bf16")
     out, lse = binding.forward(qd, H)
-    dqkv_a = binding.backward(gd, qd, out, lse, H)
-    ws = torch.full((binding.workspace_floats(B, T, H),), float("nan"), device="cuda")
+    nws = binding.workspace_floats(B, T, H)
+    ws_a = torch.full((nws,), float("nan"), device="cuda")
+    dqkv_a = torch.full_like(qd, float("nan"))
+    binding.attn_bwd(gd, qd, out, lse, dqkv_a, ws_a, H)
+    # three stages: preprocess, then dQ and dK/dV in either order
+    ws = torch.full((nws,), float("nan"), device="cuda")
     dqkv_b = torch.full_like(qd, float("nan"))
     binding.attn_bwd_preprocess(gd, out, lse, ws, H)
-    binding.attn_bwd_dq(gd, qd, ws, dqkv_b, H)     # either order is allowed
+    binding.attn_bwd_dq(gd, qd, ws, dqkv_b, H)
     binding.attn_bwd_dkdv(gd, qd, ws, dqkv_b, H)
+    # the fused first stage, then dK/dV
+    ws_c = torch.full((nws,), float("nan"), device="cuda")
+    dqkv_c = torch.full_like(qd, float("nan"))
+    binding.attn_bwd_dq_preprocess(gd, qd, out, lse, dqkv_c, ws_c, H)
+    binding.attn_bwd_dkdv(gd, qd, ws_c, dqkv_c, H)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(dqkv_a), _bits(dqkv_b))
+    assert np.array_equal(_bits(dqkv_a), _bits(dqkv_c))
+    for w_ in (ws_a, ws_c):
+        assert np.array_equal(w_.cpu().numpy().view(np.uint32), ws.cpu().numpy().view(np.uint32))
     # workspace: D = rowsum(dout * out) in float32, then LSE * log2(e); padding
     Tp = (T + 63) // 64 * 64
     w = ws.cpu().numpy().reshape(2, B, H, Tp)
