@@ -144,7 +144,7 @@ def attn_fwd(qkv, out, lse, n_head: int, head_dim: int = 64, stream=None) -> Non
 
 
 def workspace_floats(B: int, T: int, n_head: int) -> int:
-    """Floats the backward workspace must hold: 2 * B * n_head * round_up(T, 64)."""
+    """Floats the backward workspace must hold: 10 * B * n_head * round_up(T, 64)."""
     n = int(lib().attn_bwd_workspace_floats(B, T, n_head))
     if n < 0:
         raise ValueError("B, T and n_head must be non-negative")

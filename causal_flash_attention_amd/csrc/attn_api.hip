@@ -111,7 +111,7 @@ struct Sizes {
 
 long long workspace_floats(int B, int T, int H) {
     const long long tp = ((long long)T + 63) / 64 * 64;
-    return 2LL * B * H * tp;
+    return 10LL * B * H * tp;  // D, LSE*log2 e, then 32 bytes of MFMA terms per row
 }
 
 Sizes sizes(int B, int T, int H, int elem) {

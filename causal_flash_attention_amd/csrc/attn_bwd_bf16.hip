@@ -50,9 +50,35 @@ __device__ __forceinline__ float dot_half(const bf16x8 (&g)[4], const bf16x8 (&o
     return acc;
 }
 
+// The MFMA form of a row statistic x: eight bf16 [x1 x2 x3 0 0 0 0 0] with
+// x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2), so x1 + x2 + x3
+// equals x for every normal float. One extra MFMA k-step with these terms as
+// A and -1 as B subtracts x from a whole score row inside the accumulator.
+__device__ __forceinline__ u32x4 mfma_terms(float x) {
+    const bf16 a = (bf16)x;
+    const float r = x - (float)a;
+    const bf16 b = (bf16)r;
+    const bf16 c = (bf16)(r - (float)b);
+    const bf16 z = (bf16)0.0f;
+    const bf16x8 v = {a, b, c, z, z, z, z, z};
+    return __builtin_bit_cast(u32x4, v);
+}
+
+// The m terms of a row past T: the largest finite bf16, so that P = 0 there
+// while every product in the MFMA stays finite.
+__device__ __forceinline__ u32x4 mfma_terms_pad() {
+    const u32x4 v = {0x7F7Fu, 0u, 0u, 0u};
+    return v;
+}
+
+// Workspace row r's 32 bytes of MFMA terms: [m terms | D terms], m = 8 * LSE.
+__device__ __forceinline__ u32x4* ws_terms(float* ws, long long n_pad_rows) {
+    return reinterpret_cast<u32x4*>(ws + 2 * n_pad_rows);
+}
+
 // Blocks [0, nb_d): D, two lanes per (b, t, h) row (one per half).
-// Blocks [nb_d, ...): one thread per padded (bh, t): LSE * log2 e, and the
-// padding of both arrays.
+// Blocks [nb_d, ...): one thread per padded (bh, t): LSE * log2 e and the m
+// terms, and the padding of all of them.
 __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
     const bf16* __restrict__ dout, const bf16* __restrict__ out, const float* __restrict__ lse,
     float* __restrict__ ws, int T, int Tp, int H, long long n_rows, long long nb_d,
@@ -75,23 +101,30 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
             acc = dot_half(g, o);
         }
         acc += __shfl_xor(acc, 1, 64);
-        if (row < n_rows && half == 0) {
+        if (row < n_rows) {
             const long long bt = row / H;
             const int h = (int)(row - bt * H);
             const long long b = bt / T;
             const int t = (int)(bt - b * T);
-            dd[(b * H + h) * Tp + t] = acc;
+            const long long r = (b * H + h) * Tp + t;
+            if (half == 0) dd[r] = acc;
+            else ws_terms(ws, n_pad_rows)[2 * r + 1] = mfma_terms(acc);
         }
     } else {
         const long long i = (blk - nb_d) * 256 + threadIdx.x;  // padded (bh, t)
         if (i < n_pad_rows) {
             const long long bh = i / Tp;
             const int t = (int)(i - bh * Tp);
+            u32x4* terms = ws_terms(ws, n_pad_rows);
             if (t < T) {
-                lse2[i] = lse[bh * T + t] * LOG2E;
+                const float l = lse[bh * T + t];
+                lse2[i] = l * LOG2E;
+                terms[2 * i] = mfma_terms(8.0f * l);
             } else {
                 lse2[i] = INFINITY;
                 dd[i] = 0.0f;
+                terms[2 * i] = mfma_terms_pad();
+                terms[2 * i + 1] = mfma_terms(0.0f);
             }
         }
     }
@@ -100,10 +133,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV. One workgroup = 4 waves = 128 keys of one (batch, head); wave w owns
 // keys k0 + 32w .. +31, with K and V of those keys held in registers. Query
-// tiles of 64 rows (Q, dO, and their LSE*log2 e and D) stream through a
-// three-stage ring of LDS buffers filled by direct global->LDS loads. Per
-// tile and wave: S = Q K^T and dP = dO V^T on MFMA (lane l%32 owns key l%32),
-// P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS on MFMA with
+// tiles of 64 rows (Q, dO, and the MFMA terms of their 8 * LSE and D) stream
+// through a three-stage ring of LDS buffers filled by direct loads. Per tile
+// and wave: S - 8 LSE and dP - D on MFMA (lane l%32 owns key l%32; the row
+// statistics enter as one extra k-step of each product, so no lane reads
+// them), P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS on MFMA with
 // P and dS fed straight from registers and Q^T, dO^T read from the row-major
 // tiles by transposing LDS reads. Query tiles entirely before a wave's keys
 // are skipped.
@@ -114,7 +148,7 @@ constexpr int KV_BM = 64;   // queries per LDS tile
 struct alignas(16) DkdvSmem {
     bf16 q[NSTAGE][ATILE_ELEMS];
     bf16 g[NSTAGE][ATILE_ELEMS];
-    float stats[NSTAGE][2 * KV_BM];  // [LSE * log2 e | D] of the tile's queries
+    bf16 terms[NSTAGE][KV_BM * 16];  // per query row: [m terms | D terms]
 };
 
 // The dK/dV step on a 64-query tile runs as two 32-query halves (QB), each
@@ -123,9 +157,13 @@ struct alignas(16) DkdvSmem {
 // one half's VALU work sits between MFMAs of the other half that do not
 // depend on it. MASK applies the causal mask (the tile holding this wave's
 // diagonal only).
+// S - 8 LSE and dP - D of one half: four k-steps over d, then one over the
+// row's terms (A: lane half 0 holds the m terms, half 1 the D terms; B: bs
+// is -1 on the m terms and bd is -1 on the D terms, zero elsewhere).
 template <int QB>
-__device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, const bf16x8 (&kreg)[4],
-                                         const bf16x8 (&vreg)[4], const int (&roff)[4],
+__device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, lds_bf16* terms,
+                                         const bf16x8 (&kreg)[4], const bf16x8 (&vreg)[4],
+                                         const int (&roff)[4], bf16x8 bs, bf16x8 bd, int toff,
                                          f32x16& s, f32x16& dp) {
     typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
     s = zero16();
@@ -136,30 +174,25 @@ __device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, const bf16x
         s = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s);
         dp = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp);
     }
+    const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(terms + QB * 32 * 16 + toff);
+    s = mfma32(a, bs, s);
+    dp = mfma32(a, bd, dp);
 }
 
+// P = exp2(c (S - 8 LSE)) = exp(scale S - LSE) and dS = P (dP - D).
 template <int QB, bool MASK>
-__device__ __forceinline__ void dkdv_pds(__attribute__((address_space(3))) const float* stats,
-                                         f32x16& s, f32x16& dp, int lim, float c_log2, int hf,
+__device__ __forceinline__ void dkdv_pds(f32x16& s, f32x16& dp, int lim, float c_log2,
                                          bf16x8 (&pds)[4]) {
-    typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
     if (MASK) {  // query QB*32 + 8(i/4) + 4hf + (i%4) < my_k - q0  ->  P = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             if (QB * 32 + 8 * (i >> 2) + (i & 3) < lim) s[i] = -INFINITY;
     }
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-        const int qi = QB * 32 + 8 * g4 + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(stats + qi);
-        const f32x4 d4 = *reinterpret_cast<lds_f32x4*>(stats + 64 + qi);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g4 + r;
-            const float p = fast_exp2(fmaf(s[i], c_log2, -l4[r]));
-            s[i] = p;
-            dp[i] = p * (dp[i] - d4[r]);
-        }
+    for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(s[i] * c_log2);
+        s[i] = p;
+        dp[i] = p * dp[i];
     }
     pds[0] = c_rows_to_operand(s, 0);
     pds[1] = c_rows_to_operand(s, 1);
@@ -181,19 +214,18 @@ __device__ __forceinline__ void dkdv_acc(lds_bf16* qt, lds_bf16* gt, const int (
 }
 
 template <bool MASK>
-__device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt,
-                                          __attribute__((address_space(3))) const float* stats,
+__device__ __forceinline__ void dkdv_tile(lds_bf16* qt, lds_bf16* gt, lds_bf16* terms,
                                           const bf16x8 (&kreg)[4], const bf16x8 (&vreg)[4],
                                           const int (&roff)[4], const int (&troff)[2][2],
-                                          f32x16 (&dvt)[2], f32x16 (&dkt)[2], int lim,
-                                          float c_log2, int hf) {
+                                          bf16x8 bs, bf16x8 bd, int toff, f32x16 (&dvt)[2],
+                                          f32x16 (&dkt)[2], int lim, float c_log2) {
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pds0[4], pds1[4];
-    dkdv_sdp<0>(qt, gt, kreg, vreg, roff, s0, dp0);
-    dkdv_sdp<1>(qt, gt, kreg, vreg, roff, s1, dp1);
-    dkdv_pds<0, MASK>(stats, s0, dp0, lim, c_log2, hf, pds0);
+    dkdv_sdp<0>(qt, gt, terms, kreg, vreg, roff, bs, bd, toff, s0, dp0);
+    dkdv_sdp<1>(qt, gt, terms, kreg, vreg, roff, bs, bd, toff, s1, dp1);
+    dkdv_pds<0, MASK>(s0, dp0, lim, c_log2, pds0);
     dkdv_acc<0>(qt, gt, troff, pds0, dvt, dkt);
-    dkdv_pds<1, MASK>(stats, s1, dp1, lim, c_log2, hf, pds1);
+    dkdv_pds<1, MASK>(s1, dp1, lim, c_log2, pds1);
     dkdv_acc<1>(qt, gt, troff, pds1, dvt, dkt);
 }
 
@@ -225,8 +257,8 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const bf16* kbase = qbase + C;
     const bf16* vbase = qbase + 2 * C;
     const bf16* gbase = dout + (long long)b * T * C + h * HEAD_DIM;
-    const float* dd_row = ws + (long long)bh * Tp;
-    const float* lse2_row = ws + (long long)BH * Tp + (long long)bh * Tp;
+    // This head's rows of MFMA terms (32 bytes each) in the workspace.
+    const char* terms_rows = reinterpret_cast<const char*>(ws + 2LL * BH * Tp) + (long long)bh * Tp * 32;
 
     const int k0 = kt * KV_BN;
     const int kw = k0 + wave * 32;
@@ -247,14 +279,22 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const int qt_begin = k0 / KV_BM;
     const int n_it = (T + KV_BM - 1) / KV_BM - qt_begin;
 
-    const float* stats_src = (lane < 16 ? lse2_row : dd_row) + 4 * (lane & 15);
+    // Extra k-step operands: A = the row's terms (lane half 0: m, half 1: D),
+    // read at toff; B = -1 on the first three k of the matching half.
+    const int toff = l32 * 16 + hf * 8;
+    const bf16 m1 = (bf16)-1.0f, z0 = (bf16)0.0f;
+    const bf16x8 neg3 = {m1, m1, m1, z0, z0, z0, z0, z0}, zero8 = {z0, z0, z0, z0, z0, z0, z0, z0};
+    const bf16x8 bs = hf == 0 ? neg3 : zero8;
+    const bf16x8 bd = hf == 0 ? zero8 : neg3;
     // Issue the loads of query tile `it` (relative) into stage `st`: Q and dO
-    // by every wave, the row statistics by wave 0 (lanes 0..31, 16 bytes each).
+    // by every wave, the tile's 2 KB of terms by waves 0 and 1 (1 KB each).
     auto issue = [&](int it, int st) {
         const int q0 = (qt_begin + it) * KV_BM;
         atile_load(atile_addr(sm.q[st]), rows_rsrc(qbase, rs, q0, T), 0, ld_rs);
         atile_load(atile_addr(sm.g[st]), rows_rsrc(gbase, C, q0, T), 0, ld_C);
-        if (wave == 0 && lane < 32) lds_dma16(stats_src + q0, atile_addr((const bf16*)sm.stats[st]));
+        if (wave < 2)
+            lds_dma16(terms_rows + (long long)(q0 + 32 * wave) * 32 + lane * 16,
+                      atile_addr(sm.terms[st] + wave * 512));
     };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
@@ -283,7 +323,7 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     static_assert(KV_BN == 2 * KV_BM, "diagonal within the first two tiles");
     auto step = [&](int it, auto maybe_diag) {
         if (it + 1 < n_it) {
-            if (wave == 0) wait_vmem<5>();
+            if (wave < 2) wait_vmem<5>();
             else wait_vmem<4>();
         } else {
             wait_vmem<0>();
@@ -294,17 +334,18 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
         const int st = it % NSTAGE;
         lds_bf16* qt = atile_view(sm.q[st]);
         lds_bf16* gt = atile_view(sm.g[st]);
-        typedef __attribute__((address_space(3))) const float lds_f32;
-        lds_f32* stats = (lds_f32*)atile_view((const bf16*)sm.stats[st]);
+        lds_bf16* terms = atile_view(sm.terms[st]);
         const int lim = my_k - q0 - 4 * hf;
         if (decltype(maybe_diag)::value) {
             if (q0 + KV_BM - 1 < kw) return;  // every query of the tile precedes this wave's keys
             if (q0 == (kw & ~(KV_BM - 1))) {  // the tile holding this wave's diagonal
-                dkdv_tile<true>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+                dkdv_tile<true>(qt, gt, terms, kreg, vreg, roff, troff, bs, bd, toff, dvt, dkt,
+                                lim, c_log2);
                 return;
             }
         }
-        dkdv_tile<false>(qt, gt, stats, kreg, vreg, roff, troff, dvt, dkt, lim, c_log2, hf);
+        dkdv_tile<false>(qt, gt, terms, kreg, vreg, roff, troff, bs, bd, toff, dvt, dkt, lim,
+                         c_log2);
     };
     const int n_head_it = n_it < 2 ? n_it : 2;
     for (int it = 0; it < n_head_it; ++it) step(it, std::true_type());
@@ -467,10 +508,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
         const float part = dot_half(greg, oreg);  // zero past T
         dd = part + swap_halves(part);
         lse2 = q_ok ? lse[(long long)bh * T + my_q] * LOG2E : INFINITY;
-        if (hf == 0 && my_q < Tp) {
-            ws[(long long)bh * Tp + my_q] = dd;
-            ws[(long long)BH * Tp + (long long)bh * Tp + my_q] = lse2;
-        }
     } else {
         const long long ws_i = (long long)bh * Tp + min(my_q, Tp - 1);
         dd = q_ok ? ws[ws_i] : 0.0f;
@@ -494,6 +531,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
             dq_tile<true>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
         else
             dq_tile<false>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);
+    }
+
+    // The workspace rows of this workgroup, written last (the dK/dV kernel
+    // reads them after this kernel has finished): D, LSE * log2 e and their
+    // MFMA terms, with the padding past T.
+    if (FUSED_PRE && hf == 0 && my_q < Tp) {
+        const long long r = (long long)bh * Tp + my_q;
+        ws[r] = dd;
+        ws[(long long)BH * Tp + r] = lse2;
+        u32x4* terms = ws_terms(ws, (long long)BH * Tp);
+        terms[2 * r] = q_ok ? mfma_terms(8.0f * lse[(long long)bh * T + my_q]) : mfma_terms_pad();
+        terms[2 * r + 1] = mfma_terms(dd);
     }
 
     if (q_ok) {

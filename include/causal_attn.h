@@ -34,11 +34,19 @@
  *   dqkv  (B, T, 3C)  [dQ | dK | dV], mirrors qkv; overwritten, never
  *                     accumulated into
  *   delta         float32 workspace of attn_bwd_workspace_floats(B, T, n_head)
- *                 = 2 * B * n_head * Tp floats, Tp = T rounded up to a multiple
- *                 of 64: first D[b, h, t] at (b * n_head + h) * Tp + t (0 for
- *                 t >= T), then LSE * log2(e) at the same offsets plus
- *                 B * n_head * Tp (+inf for t >= T); written by the backward's
- *                 preprocess stage and read by its other two stages
+ *                 = 10 * B * n_head * Tp floats, Tp = T rounded up to a
+ *                 multiple of 64, with R = B * n_head * Tp padded rows and
+ *                 row index r = (b * n_head + h) * Tp + t:
+ *                   floats [0, R):   D[b, h, t] = sum_k dout * out (0 for t >= T)
+ *                   floats [R, 2R):  LSE * log2(e) (+inf for t >= T)
+ *                   bytes from 8R:   32 bytes per row, eight bf16 [m1 m2 m3 0 0 0
+ *                                    0 0] then eight bf16 [d1 d2 d3 0 0 0 0 0],
+ *                                    where m1 + m2 + m3 splits m = 8 * LSE and
+ *                                    d1 + d2 + d3 splits D into three bf16
+ *                                    terms of decreasing size (for t >= T:
+ *                                    m1 = the largest finite bf16, the rest 0)
+ *                 written by the backward's preprocess work and read by its
+ *                 other stages
  * Element types: the unsuffixed calls take bf16 (IEEE binary32 upper half,
  * passed as void*), accumulate in float32 and round results to nearest-even
  * bf16; the _f32 calls take and produce float32 throughout.

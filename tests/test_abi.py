@@ -128,10 +128,10 @@ def test_stage_validation(L):
 
 
 def test_workspace_size(L):
-    assert L.attn_bwd_workspace_floats(1, 64, 2) == 2 * 2 * 64
-    assert L.attn_bwd_workspace_floats(1, 65, 2) == 2 * 2 * 128
-    assert L.attn_bwd_workspace_floats(16, 1024, 12) == 2 * 16 * 12 * 1024
-    assert L.attn_bwd_workspace_floats(3, 1, 5) == 2 * 3 * 5 * 64
+    assert L.attn_bwd_workspace_floats(1, 64, 2) == 10 * 2 * 64
+    assert L.attn_bwd_workspace_floats(1, 65, 2) == 10 * 2 * 128
+    assert L.attn_bwd_workspace_floats(16, 1024, 12) == 10 * 16 * 12 * 1024
+    assert L.attn_bwd_workspace_floats(3, 1, 5) == 10 * 3 * 5 * 64
     assert L.attn_bwd_workspace_floats(0, 10, 2) == 0
     assert L.attn_bwd_workspace_floats(-1, 10, 2) == -1
 

@@ -97,7 +97,10 @@ def test_stage_entry_points_match_attn_bwd():
         assert np.array_equal(w_.cpu().numpy().view(np.uint32), ws.cpu().numpy().view(np.uint32))
     # workspace: D = rowsum(dout * out) in float32, then LSE * log2(e); padding
     Tp = (T + 63) // 64 * 64
-    w = ws.cpu().numpy().reshape(2, B, H, Tp)
+    R = B * H * Tp
+    w_all = ws.cpu().numpy()
+    assert w_all.size == 10 * R
+    w = w_all[:2 * R].reshape(2, B, H, Tp)
     g64 = I.to_float64(dout, "bf16").reshape(B, T, H, D)
     o64 = to_host64(out).reshape(B, T, H, D)
     d_ref = np.einsum("bthk,bthk->bht", g64, o64)
@@ -106,6 +109,18 @@ def test_stage_entry_points_match_attn_bwd():
     l_ref = lse.cpu().numpy().astype(np.float64) * np.log2(np.e)
     np.testing.assert_allclose(w[1, :, :, :T], l_ref, rtol=1e-6, atol=1e-6)
     assert np.all(np.isposinf(w[1, :, :, T:]))
+    # then 32 bytes per row: bf16 terms [m1 m2 m3 0 0 0 0 0 | d1 d2 d3 0 0 0 0 0]
+    # summing to m = 8 * LSE and to D; rows past T: m1 = largest finite bf16
+    bits = w_all[2 * R:].view(np.uint16).reshape(B, H, Tp, 2, 8)
+    terms = I.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.all(bits[..., 3:] == 0)
+    m_sum = terms[:, :, :, 0, :3].sum(-1)
+    d_sum = terms[:, :, :, 1, :3].sum(-1)
+    m_ref = (np.float32(8.0) * lse.cpu().numpy()).astype(np.float64)
+    np.testing.assert_allclose(m_sum[:, :, :T], m_ref, rtol=1e-7, atol=1e-30)
+    np.testing.assert_allclose(d_sum[:, :, :T], w[0, :, :, :T].astype(np.float64), rtol=1e-7, atol=1e-30)
+    assert np.all(bits[:, :, T:, 0, 0] == 0x7F7F) and np.all(bits[:, :, T:, 0, 1:] == 0)
+    assert np.all(bits[:, :, T:, 1, :] == 0)
 
 
 @pytest.mark.parametrize("dtype,T", [("bf16", 129), ("bf16", 1000), ("f32", 65)])
