@@ -14,7 +14,10 @@ kernel's average duration without slowing the first pass.
 Prints one JSON line. ``value`` is the counted causal FLOP rate of the whole
 step (forward 2*B*H*T^2*d, backward 2.5 times that); ``roofline`` describes
 the kernel with the longest average duration; ``cpu_baseline`` is the float64
-CPU oracle timed on a bounded sample of heads of the same workload.
+CPU oracle timed on a bounded sample of heads of the same workload;
+``unfused`` times the materialising path (attn_fwd_unfused + attn_bwd_unfused,
+the T x T matrices through HBM) on the same inputs, after the timed region,
+and gives its ratio to the flash-attention step.
 """
 
 from __future__ import annotations
@@ -58,6 +61,8 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default=None, help="workload name (default: the headline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-unfused", action="store_true",
+                   help="skip timing the materialising path")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -222,6 +227,49 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def time_unfused(w, qkv, dout, stream, K):
+    """The materialising path on the same inputs: 5 untimed steps, then
+    min(K, 20) steps between HIP events (fwd and bwd timed separately too)."""
+    import torch
+
+    from causal_flash_attention_amd import binding
+
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    C = H * D
+    dev = qkv.device
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    probs = torch.empty((B, H, T, binding.unfused_row_stride(T)), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.unfused_workspace_bytes(B, T, H), dtype=torch.uint8, device=dev)
+    dqkv = torch.empty_like(qkv)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        binding.attn_fwd_unfused(qkv, out, lse, probs, ws, H, D, stream)
+        if evs:
+            evs[1].record(stream)
+        binding.attn_bwd_unfused(dout, qkv, probs, dqkv, ws, H, D, stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = min(K, 20)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        step(ev[i])
+    torch.cuda.synchronize()
+    total = sum(ev[i][0].elapsed_time(ev[i][2]) for i in range(n)) / n
+    fwd = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(n)) / n
+    flops = w.counted_flops()["total"]
+    return {"ms_per_step": total, "fwd_ms": fwd, "bwd_ms": total - fwd, "steps": n,
+            "counted_tflops": flops / (total * 1e-3) / 1e12,
+            "what": "attn_fwd_unfused + attn_bwd_unfused: full T x T products, fp32 scores "
+                    "and dP, bf16 P and dS through HBM"}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -316,6 +364,8 @@ def main(argv=None):
             "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
             "kernel": dom}
 
+    unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -344,6 +394,9 @@ def main(argv=None):
         "host_wall_s": wall,
         "roofline": roof,
     }
+    if unfused is not None:
+        unfused["fa_speedup"] = unfused["ms_per_step"] / ms_per_step
+        result["unfused"] = unfused
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -13,12 +13,16 @@ from .binding import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_dq_preprocess,
     attn_bwd_preprocess,
+    attn_bwd_unfused,
     attn_fwd,
+    attn_fwd_unfused,
     attn_last_error,
     attn_status_string,
     attn_version,
     backward,
     forward,
     lib,
+    unfused_row_stride,
+    unfused_workspace_bytes,
     workspace_floats,
 )

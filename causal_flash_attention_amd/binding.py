@@ -40,6 +40,9 @@ SIGNATURES = {
     "attn_bwd_dkdv": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_dq": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_unfused_workspace_bytes": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_fwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
@@ -217,6 +220,52 @@ def attn_bwd_dkdv(dout, qkv, delta, dqkv, n_head: int, head_dim: int = 64, strea
 
 def attn_bwd_dq(dout, qkv, delta, dqkv, n_head: int, head_dim: int = 64, stream=None) -> None:
     _bwd_stage("attn_bwd_dq", dout, qkv, delta, dqkv, n_head, head_dim, stream)
+
+
+def unfused_row_stride(T: int) -> int:
+    """Row length of the materialising path's T x T matrices: round_up(T, 8)."""
+    return (T + 7) // 8 * 8
+
+
+def unfused_workspace_bytes(B: int, T: int, n_head: int) -> int:
+    """Bytes of the materialising path's workspace: 6 * B * n_head * T * round_up(T, 8)."""
+    n = int(lib().attn_unfused_workspace_bytes(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def _require_bytes(t, name: str, nbytes: int) -> None:
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} must hold at least {nbytes} bytes")
+
+
+def attn_fwd_unfused(qkv, out, lse, probs, ws, n_head: int, head_dim: int = 64,
+                     stream=None) -> None:
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _require(out, "out", torch.bfloat16, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require(probs, "probs", torch.bfloat16, (B, n_head, T, unfused_row_stride(T)))
+    _require_bytes(ws, "ws", unfused_workspace_bytes(B, T, n_head))
+    _check(lib().attn_fwd_unfused(_ptr(qkv), _ptr(out), _ptr(lse), _ptr(probs), _ptr(ws), B, T,
+                                  n_head, head_dim, _stream_ptr(stream)), "attn_fwd_unfused")
+
+
+def attn_bwd_unfused(dout, qkv, probs, dqkv, ws, n_head: int, head_dim: int = 64,
+                     stream=None) -> None:
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(dout, "dout", torch.bfloat16, (B, T, C))
+    _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _require(probs, "probs", torch.bfloat16, (B, n_head, T, unfused_row_stride(T)))
+    _require(dqkv, "dqkv", torch.bfloat16, (B, T, 3 * C))
+    _require_bytes(ws, "ws", unfused_workspace_bytes(B, T, n_head))
+    _check(lib().attn_bwd_unfused(_ptr(dout), _ptr(qkv), _ptr(probs), _ptr(dqkv), _ptr(ws), B, T,
+                                  n_head, head_dim, _stream_ptr(stream)), "attn_bwd_unfused")
 
 
 def attn_status_string(status: int) -> str:

@@ -14,6 +14,12 @@ hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, voi
                                      hipStream_t);
 hipError_t launch_attn_bwd_dq_bf16(const void*, const void*, const float*, void*, int, int, int,
                                    hipStream_t);
+hipError_t launch_attn_fwd_unfused_bf16(const void*, void*, float*, void*, void*, int, int, int,
+                                        hipStream_t);
+hipError_t launch_attn_bwd_unfused_bf16(const void*, const void*, const void*, void*, void*, int,
+                                        int, int, hipStream_t);
+int unfused_max_T();
+long long unfused_row_stride(int T);
 hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
                                        void*, int, int, int, hipStream_t);
 hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
@@ -232,6 +238,20 @@ int bwd_common(const void* dout, const void* qkv, const void* out, const float* 
     return ATTN_OK;
 }
 
+// Extra limits of the materialising path: rows of up to unfused_max_T()
+// keys held in one wave's registers by the row kernels, and one grid row per
+// head in its matrix products.
+int check_unfused(int B, int T, int H) {
+    if (T > cattn::unfused_max_T())
+        return fail(ATTN_ERR_UNSUPPORTED, "the materialising path takes T <= 4096");
+    if ((long long)B * H > 65535) return fail(ATTN_ERR_TOO_LARGE, "B*n_head exceeds 65535");
+    return ATTN_OK;
+}
+
+long long unfused_ws_bytes(int B, int T, int H) {
+    return 6LL * B * H * T * cattn::unfused_row_stride(T);
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +289,63 @@ int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqk
                 int n_head, int head_dim, void* stream) {
     return bwd_common(dout, qkv, nullptr, nullptr, dqkv, const_cast<float*>(delta), B, T, n_head,
                       head_dim, stream, 2, kDq);
+}
+
+long long attn_unfused_workspace_bytes(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    return unfused_ws_bytes(B, T, n_head);
+}
+
+int attn_fwd_unfused(const void* qkv, void* out, float* lse, void* probs, void* ws, int B, int T,
+                     int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!qkv || !out || !lse || !probs || !ws))
+        return fail(ATTN_ERR_NULL_PTR, "qkv, out, lse, probs and ws must not be NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_unfused(B, T, H)) != ATTN_OK) return st;
+    const void* al16[] = {qkv, out, probs, ws};
+    for (const void* p : al16)
+        if ((st = check_aligned(p, 16, "qkv, out, probs and ws must be 16-byte aligned")) != ATTN_OK)
+            return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const long long tt = (long long)B * H * T * cattn::unfused_row_stride(T);
+    const Span ins[] = {span(qkv, z.qkv, "qkv")};
+    const Span outs[] = {span(out, z.bt_c, "out"), span(lse, z.rows, "lse"),
+                         span(probs, tt * 2, "probs"), span(ws, tt * 4, "ws")};
+    if ((st = check_disjoint(outs, 4, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_fwd_unfused_bf16(qkv, out, lse, probs, ws, B, T, H,
+                                                             as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_fwd_unfused launch");
+}
+
+int attn_bwd_unfused(const void* dout, const void* qkv, const void* probs, void* dqkv, void* ws,
+                     int B, int T, int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!dout || !qkv || !probs || !dqkv || !ws))
+        return fail(ATTN_ERR_NULL_PTR, "dout, qkv, probs, dqkv and ws must not be NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_unfused(B, T, H)) != ATTN_OK) return st;
+    const void* al16[] = {dout, qkv, probs, dqkv, ws};
+    for (const void* p : al16)
+        if ((st = check_aligned(p, 16, "dout, qkv, probs, dqkv and ws must be 16-byte aligned")) !=
+            ATTN_OK)
+            return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const long long tt = (long long)B * H * T * cattn::unfused_row_stride(T);
+    const Span ins[] = {span(dout, z.bt_c, "dout"), span(qkv, z.qkv, "qkv"),
+                        span(probs, tt * 2, "probs")};
+    const Span outs[] = {span(dqkv, z.qkv, "dqkv"), span(ws, unfused_ws_bytes(B, T, H), "ws")};
+    if ((st = check_disjoint(outs, 2, ins, 3)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_bwd_unfused_bf16(dout, qkv, probs, dqkv, ws, B, T, H,
+                                                             as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_bwd_unfused launch");
 }
 
 long long attn_bwd_workspace_floats(int B, int T, int n_head) {

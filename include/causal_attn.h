@@ -138,6 +138,33 @@ int attn_bwd_f32(const float* dout, const float* qkv, const float* out,
                  const float* lse, float* dqkv, float* delta,
                  int B, int T, int n_head, int head_dim, void* stream);
 
+/* ------------------------------------------------ materialising (bf16) ---- */
+
+/* The same attention computed the way a framework does without flash
+ * attention, kept as the reference point for it (the pages credit flash
+ * attention with a GPT-2 124M step going from 130 ms to 96 ms: "Let's
+ * reproduce GPT-2 (124M)", chapter list, 01:48:15 to 02:00:18). Every
+ * product runs over the whole T x T square and the scores and
+ * probabilities go through HBM:
+ *   attn_fwd_unfused: S = QK^T / sqrt(d) as float32 into ws; P =
+ *     softmax_rows(causal mask(S)) as bf16 into probs (B, n_head, T, Tp8),
+ *     Tp8 = T rounded up to a multiple of 8, with P = 0 above the diagonal
+ *     and in the padding columns; lse as for attn_fwd; out = P V.
+ *   attn_bwd_unfused: dP = dout V^T as float32 into ws, then dS = P (dP -
+ *     rowsum(P dP)) as bf16 after it; dQ = dS K / sqrt(d), dK = dS^T Q /
+ *     sqrt(d), dV = P^T dout into dqkv. probs must come from
+ *     attn_fwd_unfused on the same qkv.
+ * Same layouts, dtypes, status codes and ownership rules as attn_fwd /
+ * attn_bwd; ws is a caller-owned device buffer of
+ * attn_unfused_workspace_bytes(B, T, n_head) = 6 * B * n_head * T * Tp8
+ * bytes. Extra limits: T <= 4096 (ATTN_ERR_UNSUPPORTED) and
+ * B * n_head <= 65535 (ATTN_ERR_TOO_LARGE). */
+long long attn_unfused_workspace_bytes(int B, int T, int n_head);
+int attn_fwd_unfused(const void* qkv, void* out, float* lse, void* probs, void* ws,
+                     int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_unfused(const void* dout, const void* qkv, const void* probs, void* dqkv,
+                     void* ws, int B, int T, int n_head, int head_dim, void* stream);
+
 /* ------------------------------------------------------------- status ---- */
 
 /* Static, human-readable name of a status code (never NULL). */

@@ -44,6 +44,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
               "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess", "attn_bwd_workspace_floats",
+              "attn_fwd_unfused", "attn_bwd_unfused", "attn_unfused_workspace_bytes",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -125,6 +126,34 @@ def test_stage_validation(L):
     assert L.attn_bwd_dq_preprocess(G, Q, None, LS, DQ, DL, *ok, None) == -1   # needs out
     assert L.attn_bwd_dq_preprocess(G, Q, O, LS, DQ, DQ + 64, *ok, None) == -6  # delta in dqkv
     assert L.attn_bwd_dq_preprocess(G, Q, O, LS, DQ, DL + 4, *ok, None) == -5
+
+
+@no_gpu_only
+def test_unfused_validation(L):
+    ok = (1, 64, 2, 64)
+    P, W = 0x70000000, 0x80000000
+    f, g = L.attn_fwd_unfused, L.attn_bwd_unfused
+    assert f(Q, O, LS, P, None, *ok, None) == -1
+    assert f(Q, O, LS, None, W, *ok, None) == -1
+    assert f(Q, O, LS, P, W, 1, 4097, 2, 64, None) == -3       # T above 4096
+    assert f(Q, O, LS, P, W, 300, 64, 300, 64, None) == -4     # B * n_head above 65535
+    assert f(Q, O, LS, P, W, 1, 64, 2, 32, None) == -3
+    assert f(Q, O, LS, P + 8, W, *ok, None) == -5
+    assert f(Q, O, LS, Q + 64, W, *ok, None) == -6             # probs inside qkv
+    assert f(Q, O, LS, P, P + 64, *ok, None) == -6             # ws inside probs
+    assert g(G, Q, P, DQ, None, *ok, None) == -1
+    assert g(G, Q, P, DQ, W + 4, *ok, None) == -5
+    assert g(G, Q, P, P + 32, W, *ok, None) == -6              # dqkv overlaps probs
+    assert g(G, Q, P, DQ, W, 1, 5000, 1, 64, None) == -3
+    for fn in (f, g):
+        assert fn(None, None, None, None, None, 0, 64, 2, 64, None) == 0
+
+
+def test_unfused_workspace_size(L):
+    assert L.attn_unfused_workspace_bytes(16, 1024, 12) == 6 * 16 * 12 * 1024 * 1024
+    assert L.attn_unfused_workspace_bytes(1, 1, 1) == 6 * 8         # rows padded to 8
+    assert L.attn_unfused_workspace_bytes(2, 13, 3) == 6 * 2 * 3 * 13 * 16
+    assert L.attn_unfused_workspace_bytes(-1, 1, 1) == -1
 
 
 def test_workspace_size(L):
