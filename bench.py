@@ -17,7 +17,9 @@ the kernel with the longest average duration; ``cpu_baseline`` is the float64
 CPU oracle timed on a bounded sample of heads of the same workload;
 ``unfused`` times the materialising path (attn_fwd_unfused + attn_bwd_unfused,
 the T x T matrices through HBM) on the same inputs, after the timed region,
-and gives its ratio to the flash-attention step.
+and gives its ratio to the flash-attention step; ``decode`` times attn_decode
+over a K/V cache larger than the Infinity Cache and reports its HBM rate
+against the 8 TB/s roofline.
 """
 
 from __future__ import annotations
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "causal attention fwd+bwd TFLOP/s at GPT-2 124M shape; % of bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD specification
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD specification
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "causal_flash_attention_amd", "csrc")
 
@@ -63,6 +66,7 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true",
                    help="skip timing the materialising path")
+    p.add_argument("--no-decode", action="store_true", help="skip timing decode")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -270,6 +274,44 @@ def time_unfused(w, qkv, dout, stream, K):
                     "and dP, bf16 P and dS through HBM"}
 
 
+# Decode workload: GPT-2 124M heads, batch 64, 4096 cached positions in
+# separate (B, T, C) caches: 805 MB of K and V per call, three times the
+# 256 MB Infinity Cache, so repeated calls stream from HBM.
+DECODE_B, DECODE_T, DECODE_H = 64, 4096, 12
+
+
+def time_decode(stream, calls=50):
+    import torch
+
+    from causal_flash_attention_amd import binding
+
+    B, T, H, D = DECODE_B, DECODE_T, DECODE_H, 64
+    C = H * D
+    g = torch.Generator(device="cuda").manual_seed(0)  # synthetic, seeded
+    k = torch.randn((B, T, C), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, T, C), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, C), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(binding.decode_workspace_floats(B, T, H), device="cuda")
+    for _ in range(10):
+        binding.attn_decode(q, k, v, out, lse, ws, T, H, D, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        binding.attn_decode(q, k, v, out, lse, ws, T, H, D, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / calls
+    nbytes = 2.0 * B * T * C * 2  # K and V read once
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"decode B={B} T={T} n_head={H} head_dim={D}, separate K/V caches",
+            "us_per_call": us, "calls": calls, "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS}}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -365,6 +407,7 @@ def main(argv=None):
             "kernel": dom}
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
+    decode = None if args.no_decode else time_decode(stream)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -397,6 +440,8 @@ def main(argv=None):
     if unfused is not None:
         unfused["fa_speedup"] = unfused["ms_per_step"] / ms_per_step
         result["unfused"] = unfused
+    if decode is not None:
+        result["decode"] = decode
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

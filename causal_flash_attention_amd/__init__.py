@@ -14,12 +14,14 @@ from .binding import (  # noqa: F401
     attn_bwd_dq_preprocess,
     attn_bwd_preprocess,
     attn_bwd_unfused,
+    attn_decode,
     attn_fwd,
     attn_fwd_unfused,
     attn_last_error,
     attn_status_string,
     attn_version,
     backward,
+    decode_workspace_floats,
     forward,
     lib,
     unfused_row_stride,

@@ -42,6 +42,9 @@ SIGNATURES = {
     "attn_bwd_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
     "attn_unfused_workspace_bytes": ([_I, _I, _I], ctypes.c_longlong),
     "attn_fwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_decode_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_decode": ([_P, ctypes.c_longlong, _P, _P, ctypes.c_longlong, ctypes.c_longlong,
+                     _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
@@ -266,6 +269,44 @@ def attn_bwd_unfused(dout, qkv, probs, dqkv, ws, n_head: int, head_dim: int = 64
     _require_bytes(ws, "ws", unfused_workspace_bytes(B, T, n_head))
     _check(lib().attn_bwd_unfused(_ptr(dout), _ptr(qkv), _ptr(probs), _ptr(dqkv), _ptr(ws), B, T,
                                   n_head, head_dim, _stream_ptr(stream)), "attn_bwd_unfused")
+
+
+def decode_workspace_floats(B: int, T: int, n_head: int) -> int:
+    """Floats of the decode workspace for this shape."""
+    n = int(lib().attn_decode_workspace_floats(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def attn_decode(q, k_cache, v_cache, out, lse, ws, T: int, n_head: int, head_dim: int = 64,
+                stream=None) -> None:
+    """q: (B, C) bf16 view with unit stride along C; k_cache, v_cache:
+    (B, T_max, C) bf16 views with unit stride along C (any row and batch
+    strides, e.g. slices of a packed qkv); positions 0 .. T-1 are used."""
+    torch = _torch()
+    C = n_head * head_dim
+    for t, name, dim in ((q, "q", 2), (k_cache, "k_cache", 3), (v_cache, "v_cache", 3)):
+        if t is None or not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != dim:
+            raise ValueError(f"{name} must be a {dim}-D bfloat16 GPU tensor")
+        if t.shape[-1] != C or t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a last dimension of {C} with unit stride")
+    B = int(q.shape[0])
+    if k_cache.shape[0] != B or v_cache.shape[0] != B:
+        raise ValueError("q, k_cache and v_cache must share the batch dimension")
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same strides")
+    if not 0 <= T <= min(k_cache.shape[1], v_cache.shape[1]):
+        raise ValueError("T exceeds the cache length")
+    _require(out, "out", torch.bfloat16, (B, C))
+    _require(lse, "lse", torch.float32, (B, n_head))
+    n = decode_workspace_floats(B, T, n_head)
+    if ws is None or not ws.is_cuda or ws.dtype != torch.float32 or not ws.is_contiguous() \
+            or ws.numel() < n:
+        raise ValueError(f"ws must be a contiguous float32 GPU tensor of at least {n} floats")
+    _check(lib().attn_decode(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache),
+                             k_cache.stride(1), k_cache.stride(0), _ptr(out), _ptr(lse), _ptr(ws),
+                             B, T, n_head, head_dim, _stream_ptr(stream)), "attn_decode")
 
 
 def attn_status_string(status: int) -> str:

@@ -19,6 +19,9 @@ hipError_t launch_attn_fwd_unfused_bf16(const void*, void*, float*, void*, void*
 hipError_t launch_attn_bwd_unfused_bf16(const void*, const void*, const void*, void*, void*, int,
                                         int, int, hipStream_t);
 int unfused_max_T();
+long long decode_workspace_floats(int B, int T, int H);
+hipError_t launch_attn_decode_bf16(const void*, long long, const void*, const void*, long long,
+                                   long long, void*, float*, float*, int, int, int, hipStream_t);
 long long unfused_row_stride(int T);
 hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
                                        void*, int, int, int, hipStream_t);
@@ -346,6 +349,54 @@ int attn_bwd_unfused(const void* dout, const void* qkv, const void* probs, void*
     const hipError_t e = cattn::launch_attn_bwd_unfused_bf16(dout, qkv, probs, dqkv, ws, B, T, H,
                                                              as_stream(stream));
     return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_bwd_unfused launch");
+}
+
+long long attn_decode_workspace_floats(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    return cattn::decode_workspace_floats(B, T, n_head);
+}
+
+int attn_decode(const void* q, long long q_batch_stride, const void* k_cache, const void* v_cache,
+                long long cache_row_stride, long long cache_batch_stride, void* out, float* lse,
+                float* ws, int B, int T, int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!q || !k_cache || !v_cache || !out || !lse || !ws))
+        return fail(ATTN_ERR_NULL_PTR, "q, k_cache, v_cache, out, lse and ws must not be NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((long long)B * H > 65535) return fail(ATTN_ERR_TOO_LARGE, "B*n_head exceeds 65535");
+    const long long C = (long long)H * head_dim;
+    if (q_batch_stride < C || cache_row_stride < C ||
+        (B > 1 && cache_batch_stride < (long long)(T - 1) * cache_row_stride + C))
+        return fail(ATTN_ERR_BAD_SHAPE, "strides smaller than the rows they step over");
+    if (q_batch_stride % 8 || cache_row_stride % 8 || cache_batch_stride % 8)
+        return fail(ATTN_ERR_MISALIGNED, "strides must be multiples of 8 elements");
+    const long long max_elems = (long long)1 << 61;
+    if (cache_batch_stride > max_elems / (B > 0 ? B : 1) || cache_row_stride > max_elems / T ||
+        q_batch_stride > max_elems / B)
+        return fail(ATTN_ERR_TOO_LARGE, "cache extent overflows");
+    const void* al16[] = {q, k_cache, v_cache, out, ws};
+    for (const void* p : al16)
+        if ((st = check_aligned(p, 16, "q, k_cache, v_cache, out and ws must be 16-byte aligned")) !=
+            ATTN_OK)
+            return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const long long cache_elems = (long long)(B - 1) * cache_batch_stride +
+                                  (long long)(T - 1) * cache_row_stride + C;
+    const Span ins[] = {span(q, ((long long)(B - 1) * q_batch_stride + C) * 2, "q"),
+                        span(k_cache, cache_elems * 2, "k_cache"),
+                        span(v_cache, cache_elems * 2, "v_cache")};
+    const Span outs[] = {span(out, (long long)B * C * 2, "out"),
+                         span(lse, (long long)B * H * 4, "lse"),
+                         span(ws, cattn::decode_workspace_floats(B, T, H) * 4, "ws")};
+    if ((st = check_disjoint(outs, 3, ins, 3)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_decode_bf16(q, q_batch_stride, k_cache, v_cache,
+                                                        cache_row_stride, cache_batch_stride, out,
+                                                        lse, ws, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_decode launch");
 }
 
 long long attn_bwd_workspace_floats(int B, int T, int n_head) {

@@ -165,6 +165,35 @@ int attn_fwd_unfused(const void* qkv, void* out, float* lse, void* probs, void* 
 int attn_bwd_unfused(const void* dout, const void* qkv, const void* probs, void* dqkv,
                      void* ws, int B, int T, int n_head, int head_dim, void* stream);
 
+/* ---------------------------------------------------------- decode (bf16) ---- */
+
+/* One new query per (batch, head) against the keys and values of T cached
+ * positions, its own included (so no mask): the token-by-token sampling
+ * loop ("Let's reproduce GPT-2 (124M)", chapter list, 00:37:02). Per (b, h):
+ * O = sum_t softmax_t(q . k_t / sqrt(d)) v_t and LSE = ln sum_t exp(q . k_t /
+ * sqrt(d)), in float32 arithmetic.
+ *   q        bf16; element (b, h, k) at q[b * q_batch_stride + h * head_dim + k]
+ *   k_cache, v_cache
+ *            bf16; element (b, t, h, k) at
+ *            cache[b * cache_batch_stride + t * cache_row_stride + h * head_dim + k]
+ *            for t = 0 .. T-1 (position T-1 is the new token, appended by
+ *            the caller). Strides count elements and are multiples of 8. The
+ *            packed qkv of attn_fwd can serve directly: k_cache = qkv + C,
+ *            v_cache = qkv + 2C, row stride 3C, batch stride T_max * 3C.
+ *   out      (B, C) bf16
+ *   lse      (B, n_head) float32
+ *   ws       float32 workspace of attn_decode_workspace_floats(B, T, n_head)
+ * Two kernels on `stream` (split over the cache, then a fixed-order merge;
+ * the result does not depend on anything but the inputs). Limits:
+ * B * n_head <= 65535; q_batch_stride and cache_row_stride >= C; for B > 1,
+ * cache_batch_stride >= (T - 1) * cache_row_stride + C. */
+long long attn_decode_workspace_floats(int B, int T, int n_head);
+int attn_decode(const void* q, long long q_batch_stride,
+                const void* k_cache, const void* v_cache,
+                long long cache_row_stride, long long cache_batch_stride,
+                void* out, float* lse, float* ws,
+                int B, int T, int n_head, int head_dim, void* stream);
+
 /* ------------------------------------------------------------- status ---- */
 
 /* Static, human-readable name of a status code (never NULL). */

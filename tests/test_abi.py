@@ -45,6 +45,7 @@ def test_header_declares_expected_entry_points():
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
               "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess", "attn_bwd_workspace_floats",
               "attn_fwd_unfused", "attn_bwd_unfused", "attn_unfused_workspace_bytes",
+              "attn_decode", "attn_decode_workspace_floats",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -154,6 +155,32 @@ def test_unfused_workspace_size(L):
     assert L.attn_unfused_workspace_bytes(1, 1, 1) == 6 * 8         # rows padded to 8
     assert L.attn_unfused_workspace_bytes(2, 13, 3) == 6 * 2 * 3 * 13 * 16
     assert L.attn_unfused_workspace_bytes(-1, 1, 1) == -1
+
+
+@no_gpu_only
+def test_decode_validation(L):
+    f = L.attn_decode
+    K, V, W = 0x70000000, 0x80000000, 0x90000000
+    C = 128                                   # n_head 2, head_dim 64
+    assert f(None, C, K, V, 3 * C, 64 * 3 * C, O, LS, W, 1, 64, 2, 64, None) == -1
+    assert f(Q, C, K, V, 3 * C, 64 * 3 * C, O, LS, None, 1, 64, 2, 64, None) == -1
+    assert f(Q, C, K, V, 3 * C, 64 * 3 * C, O, LS, W, 1, 64, 2, 32, None) == -3
+    assert f(Q, C, K, V, 3 * C, 64 * 3 * C, O, LS, W, 300, 64, 300, 64, None) == -4
+    assert f(Q, C - 8, K, V, 3 * C, 64 * 3 * C, O, LS, W, 2, 64, 2, 64, None) == -2   # q stride < C
+    assert f(Q, C, K, V, C - 8, 64 * 3 * C, O, LS, W, 2, 64, 2, 64, None) == -2       # row stride < C
+    assert f(Q, C, K, V, 3 * C, 3 * C, O, LS, W, 2, 64, 2, 64, None) == -2            # batch rows overlap
+    assert f(Q, C, K, V, 3 * C + 4, 64 * 3 * C, O, LS, W, 1, 64, 2, 64, None) == -5   # stride not 8k
+    assert f(Q + 8, C, K, V, 3 * C, 64 * 3 * C, O, LS, W, 1, 64, 2, 64, None) == -5
+    assert f(Q, C, K, V, 3 * C, 64 * 3 * C, K + 64, LS, W, 1, 64, 2, 64, None) == -6  # out in cache
+    assert f(Q, C, K, V, 3 * C, 64 * 3 * C, O, LS, O, 1, 64, 2, 64, None) == -6       # ws is out
+    assert f(None, C, None, None, 3 * C, 0, None, None, None, 0, 64, 2, 64, None) == 0
+
+
+def test_decode_workspace_size(L):
+    assert L.attn_decode_workspace_floats(16, 1024, 12) > 0
+    assert L.attn_decode_workspace_floats(1, 1, 1) == 66            # one split: m, l, 64 sums
+    assert L.attn_decode_workspace_floats(0, 5, 2) == 0
+    assert L.attn_decode_workspace_floats(1, -1, 2) == -1
 
 
 def test_workspace_size(L):
