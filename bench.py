@@ -53,6 +53,8 @@ KERNELS = {
     "attn_bwd_dkdv": ("attn_bwd_bf16.hip", "mfma", 4.0),
 }
 STAGES = list(KERNELS)
+# Kernels outside the step whose HBM traffic is also recorded: the decode pass.
+EXTRA_TRAFFIC = {"decode_partial": ("attn_decode_bf16.hip",)}
 
 
 def parse_args(argv=None):
@@ -122,11 +124,21 @@ def _csv_rows(d: str, suffix: str):
 def _kernel_of(name: str):
     if "attn_bwd_dq_bf16_kernel" in name:  # <true>: the fused form attn_bwd launches
         return "attn_bwd_dq_preprocess" if ("<true>" in name or "ILb1E" in name) else "attn_bwd_dq"
+    m = re.search(r"gemm_bf16_kernel<(\d), (\d), (\d+), (true|false)>", name)
+    if m:  # materialising path: operand orientations, output tile width, output type
+        ori = "".join("r" if x == "0" else "t" for x in m.group(1, 2))
+        return f"unfused_gemm_{ori}{m.group(3)}_{'f32' if m.group(4) == 'true' else 'bf16'}"
+    for k, tag in (("unfused_softmax_bwd", "softmax_bwd_rows_kernel"),
+                   ("unfused_softmax", "softmax_rows_kernel"),
+                   ("decode_partial", "decode_partial_kernel"),
+                   ("decode_combine", "decode_combine_kernel")):
+        if tag in name:
+            return k
     for k, tag in (("attn_fwd", "attn_fwd_bf16_kernel"), ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
                    ("attn_bwd_dkdv", "attn_bwd_dkdv_bf16_kernel")):
         if tag in name:
             return k
-    if "copyBuffer" in name or "copy" in name.lower():
+    if "copyBuffer" in name:  # the runtime's device copy of --copy-calibration
         return "copy"
     return None
 
@@ -167,14 +179,14 @@ def write_profiles(args, w) -> int:
             raise SystemExit("the counter runs need --copy-calibration (a plain copy of known size)")
         f_fetch = COPY_BYTES / (fetch["copy"] * 1024.0)
         f_write = COPY_BYTES / (write["copy"] * 1024.0)
-        for k in KERNELS:
+        for k in list(KERNELS) + list(EXTRA_TRAFFIC):
             if k not in fetch or k not in write:
                 continue
             traffic = fetch[k] * 1024.0 * f_fetch + write[k] * 1024.0 * f_write
             text = "\n".join([
                 f"# HBM traffic of {k} on workload {w.name}, from rocprofv3 counters",
                 f"# command: {cmd}",
-                f"source_sha256_16: {source_digest(os.path.join(CSRC, KERNELS[k][0]))}",
+                f"source_sha256_16: {source_digest(os.path.join(CSRC, (KERNELS.get(k) or EXTRA_TRAFFIC[k])[0]))}",
                 f"fetch_kib_per_dispatch: {fetch[k]:.1f}",
                 f"write_kib_per_dispatch: {write[k]:.1f}",
                 f"copy_calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE "
@@ -288,9 +300,9 @@ def time_decode(stream, calls=50):
     B, T, H, D = DECODE_B, DECODE_T, DECODE_H, 64
     C = H * D
     g = torch.Generator(device="cuda").manual_seed(0)  # synthetic, seeded
-    k = torch.randn((B, T, C), generator=g, device="cuda").to(torch.bfloat16)
-    v = torch.randn((B, T, C), generator=g, device="cuda").to(torch.bfloat16)
-    q = torch.randn((B, C), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, T, C), generator=g, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((B, T, C), generator=g, device="cuda", dtype=torch.bfloat16)
+    q = torch.randn((B, C), generator=g, device="cuda", dtype=torch.bfloat16)
     out = torch.empty((B, C), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(binding.decode_workspace_floats(B, T, H), device="cuda")
