@@ -16,13 +16,17 @@ from .binding import (  # noqa: F401
     attn_bwd_unfused,
     attn_decode,
     attn_fwd,
+    attn_fwd_fp8,
     attn_fwd_unfused,
     attn_last_error,
+    attn_quantize_fp8,
     attn_status_string,
     attn_version,
     backward,
     decode_workspace_floats,
     forward,
+    forward_fp8,
+    fp8_buffer_bytes,
     lib,
     unfused_row_stride,
     unfused_workspace_bytes,

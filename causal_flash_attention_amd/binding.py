@@ -46,6 +46,9 @@ SIGNATURES = {
     "attn_decode": ([_P, ctypes.c_longlong, _P, _P, ctypes.c_longlong, ctypes.c_longlong,
                      _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_fp8_buffer_bytes": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_quantize_fp8": ([_P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_fwd_fp8": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
@@ -309,6 +312,41 @@ def attn_decode(q, k_cache, v_cache, out, lse, ws, T: int, n_head: int, head_dim
                              B, T, n_head, head_dim, _stream_ptr(stream)), "attn_decode")
 
 
+def fp8_buffer_bytes(B: int, T: int, n_head: int) -> int:
+    """Bytes of the FP8 buffer of attn_quantize_fp8 / attn_fwd_fp8."""
+    n = int(lib().attn_fp8_buffer_bytes(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def attn_quantize_fp8(qkv, fp8, n_head: int, head_dim: int = 64, stream=None) -> None:
+    """qkv: packed (B, T, 3C) bf16; fp8: contiguous GPU buffer of at least
+    fp8_buffer_bytes(B, T, n_head) bytes (any dtype, e.g. uint8)."""
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _require_bytes(fp8, "fp8", fp8_buffer_bytes(B, T, n_head))
+    _check(lib().attn_quantize_fp8(_ptr(qkv), _ptr(fp8), B, T, n_head, head_dim,
+                                   _stream_ptr(stream)), "attn_quantize_fp8")
+
+
+def attn_fwd_fp8(fp8, out, lse, n_head: int, head_dim: int = 64, stream=None) -> None:
+    """fp8: the buffer written by attn_quantize_fp8 for these shapes; out
+    (B, T, C) bf16 and lse (B, n_head, T) float32 give B and T."""
+    torch = _torch()
+    if out is None or out.dim() != 3:
+        raise ValueError("out must be a (B, T, C) tensor")
+    B, T, C = (int(x) for x in out.shape)
+    if C != n_head * head_dim:
+        raise ValueError("out's last dimension must be n_head * head_dim")
+    _require(out, "out", torch.bfloat16, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require_bytes(fp8, "fp8", fp8_buffer_bytes(B, T, n_head))
+    _check(lib().attn_fwd_fp8(_ptr(fp8), _ptr(out), _ptr(lse), B, T, n_head, head_dim,
+                              _stream_ptr(stream)), "attn_fwd_fp8")
+
+
 def attn_status_string(status: int) -> str:
     return lib().attn_status_string(status).decode()
 
@@ -332,6 +370,19 @@ def forward(qkv, n_head: int, head_dim: int = 64, stream=None):
     out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
     lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
     attn_fwd(qkv, out, lse, n_head, head_dim, stream)
+    return out, lse
+
+
+def forward_fp8(qkv, n_head: int, head_dim: int = 64, stream=None):
+    """Returns (out, lse) of the FP8 forward for a packed (B, T, 3C) bf16 GPU
+    tensor: attn_quantize_fp8 into a new buffer, then attn_fwd_fp8."""
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    fp8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device=qkv.device)
+    lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+    attn_quantize_fp8(qkv, fp8, n_head, head_dim, stream)
+    attn_fwd_fp8(fp8, out, lse, n_head, head_dim, stream)
     return out, lse
 
 

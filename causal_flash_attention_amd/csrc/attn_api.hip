@@ -25,6 +25,9 @@ hipError_t launch_attn_decode_bf16(const void*, long long, const void*, const vo
 long long unfused_row_stride(int T);
 hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
                                        void*, int, int, int, hipStream_t);
+long long fp8_buffer_bytes(int B, int T, int H);
+hipError_t launch_attn_quantize_fp8(const void*, void*, int, int, int, hipStream_t);
+hipError_t launch_attn_fwd_fp8(const void*, void*, float*, int, int, int, hipStream_t);
 hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
 hipError_t launch_attn_bwd_pre_f32(const float*, const float*, const float*, float*, int, int, int,
                                    hipStream_t);
@@ -251,6 +254,14 @@ int check_unfused(int B, int T, int H) {
     return ATTN_OK;
 }
 
+// Extra limit of the FP8 path: one head's codes (64 * round_up(T, 64) bytes)
+// are addressed with 32-bit buffer offsets.
+int check_fp8(int T) {
+    if (((long long)T + 63) / 64 * 64 * 64 > 0xffffffffLL)
+        return fail(ATTN_ERR_TOO_LARGE, "the FP8 path takes round_up(T, 64) * 64 < 2^32");
+    return ATTN_OK;
+}
+
 long long unfused_ws_bytes(int B, int T, int H) {
     return 6LL * B * H * T * cattn::unfused_row_stride(T);
 }
@@ -397,6 +408,53 @@ int attn_decode(const void* q, long long q_batch_stride, const void* k_cache, co
                                                         cache_row_stride, cache_batch_stride, out,
                                                         lse, ws, B, T, H, as_stream(stream));
     return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_decode launch");
+}
+
+long long attn_fp8_buffer_bytes(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    return cattn::fp8_buffer_bytes(B, T, n_head);
+}
+
+int attn_quantize_fp8(const void* qkv, void* fp8, int B, int T, int n_head, int head_dim,
+                      void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!qkv || !fp8))
+        return fail(ATTN_ERR_NULL_PTR, !qkv ? "qkv is NULL" : "fp8 is NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_fp8(T)) != ATTN_OK) return st;
+    if ((st = check_aligned(qkv, 16, "qkv must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(fp8, 16, "fp8 must be 16-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const Span ins[] = {span(qkv, z.qkv, "qkv")};
+    const Span outs[] = {span(fp8, cattn::fp8_buffer_bytes(B, T, H), "fp8")};
+    if ((st = check_disjoint(outs, 1, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_quantize_fp8(qkv, fp8, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_quantize_fp8 launch");
+}
+
+int attn_fwd_fp8(const void* fp8, void* out, float* lse, int B, int T, int n_head, int head_dim,
+                 void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!fp8 || !out || !lse))
+        return fail(ATTN_ERR_NULL_PTR, !fp8 ? "fp8 is NULL" : !out ? "out is NULL" : "lse is NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_fp8(T)) != ATTN_OK) return st;
+    if ((st = check_aligned(fp8, 16, "fp8 must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(out, 16, "out must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const Span ins[] = {span(fp8, cattn::fp8_buffer_bytes(B, T, H), "fp8")};
+    const Span outs[] = {span(out, z.bt_c, "out"), span(lse, z.rows, "lse")};
+    if ((st = check_disjoint(outs, 2, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_fwd_fp8(fp8, out, lse, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_fwd_fp8 launch");
 }
 
 long long attn_bwd_workspace_floats(int B, int T, int n_head) {

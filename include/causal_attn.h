@@ -194,6 +194,47 @@ int attn_decode(const void* q, long long q_batch_stride,
                 void* out, float* lse, float* ws,
                 int B, int T, int n_head, int head_dim, void* stream);
 
+/* ------------------------------------------------------------ FP8 (MXFP8) ---- */
+
+/* Causal attention forward with FP8 operands. The llm.c page ("Réimplémenter
+ * à bas coût le modèle GPT-2 avec llm.c", FAQ) has BF16 training today and
+ * FP8 planned, without a recipe; this is the variant defined here:
+ *   - OCP E4M3 elements (round to nearest even) sharing, per block of 32, an
+ *     E8M0 scale 2^e with e the smallest integer such that the block's
+ *     largest magnitude is <= 448 * 2^e (no element saturates; an all-zero
+ *     block takes e = -127). Q and K blocks run along channels, V blocks
+ *     along positions (32 aligned positions of one channel, zero past T).
+ *   - z = log2(e) * Q^ K^T / sqrt(d) (dequantized operands, causal); per row
+ *     an integer reference m = ceil(max z); weights P^ = E4M3(2^(z - m + 8))
+ *     * 2^-8; O = P^ V^ / rowsum(P^) in bf16; LSE = ln 2 (m + log2 rowsum(P^))
+ *     in float32, the log-normaliser of the weights O uses.
+ * attn_quantize_fp8 reads the packed bf16 qkv of attn_fwd and writes the FP8
+ * buffer `fp8` (caller-owned device memory of attn_fp8_buffer_bytes(B, T,
+ * n_head) bytes, 16-byte aligned). With BH = B * n_head, Tp = round_up(T, 64)
+ * and NT = Tp / 64 its layout is
+ *   [0, 64 BH Tp)          Q codes, [BH][Tp][64]
+ *   [64 BH Tp, 128 BH Tp)  K codes, [BH][Tp][64]
+ *   [128 BH Tp, 192 BH Tp) V codes, [BH][64][Tp] (channel-major)
+ *   then BH * NT tiles of 384 exponent bytes (e + 127): per tile of 64
+ *   positions, bytes [0, 128) hold Q's (position p, channel block c at
+ *   2p + c), [128, 256) K's likewise, [256, 384) V's (position block c of the
+ *   tile, channel k at 64c + k); positions in [T, Tp) are zero codes with
+ *   exponent byte 0.
+ * attn_fwd_fp8 reads that buffer and writes out (B, T, C) bf16 and lse
+ * (B, n_head, T) float32 as attn_fwd does. Both are single kernels on
+ * `stream`, allocate nothing and return the status codes above; extra limit
+ * round_up(T, 64) * 64 < 2^32 (ATTN_ERR_TOO_LARGE). The forward assumes
+ * |q . k| / sqrt(d) * log2(e) < 2^22 for every score (far beyond attention
+ * logits in practice); larger scores can give NaN. The FP8 matrix products
+ * sum their 64 exact products with about 14 significant bits (measured), so
+ * the results differ from an exact evaluation of the definition where a
+ * weight's argument lies within that error of an E4M3 rounding midpoint. */
+long long attn_fp8_buffer_bytes(int B, int T, int n_head);
+int attn_quantize_fp8(const void* qkv, void* fp8, int B, int T, int n_head, int head_dim,
+                      void* stream);
+int attn_fwd_fp8(const void* fp8, void* out, float* lse, int B, int T, int n_head, int head_dim,
+                 void* stream);
+
 /* ------------------------------------------------------------- status ---- */
 
 /* Static, human-readable name of a status code (never NULL). */

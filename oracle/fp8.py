@@ -45,9 +45,10 @@ Step 5 makes every rescale between two integer references an exact power of
 two, and E4M3 rounding commutes with powers of two in its normal range, so a
 streaming kernel whose running reference only grows reaches the same P^ as
 step 6 except (a) for probabilities below 2^-13 (E4M3 subnormals at one of
-the two references) and (b) where the float32 logit puts 2^(z - m + 8) on the
-other side of a rounding midpoint. ``rounding_slack`` bounds what those two
-cases can change.
+the two references) and (b) where the kernel's logit, computed with rounding
+error, puts 2^(z - m + 8) on the other side of a rounding midpoint.
+``rounding_slack`` bounds what those two cases can change, given a bound on
+that rounding error.
 
 Pins: tests/test_oracle_fp8.py checks the encoding against the OFP8 table and
 brute-force nearest rounding, the scale rule against its defining inequality,
@@ -252,21 +253,25 @@ def _e4m3_neighbours(x: np.ndarray):
     return lo, hi
 
 
-def rounding_slack(parts: dict, z_rel: float = 2.0 ** -20):
-    """Per-row bounds on what a float32 streaming kernel may legitimately
-    differ from head_forward_fp8 by, through the two cases named in the module
-    docstring: (a) probabilities 2^(z - m) below 2^-13, whose codes depend on
-    the reference in use (each may move by at most 2^-17 after the final
-    rescale), and (b) codes whose argument 2^(z - m + 8) lies within relative
-    ``z_rel`` of a rounding midpoint (each may move by one grid step). z_rel
-    covers the float32 error of the logit (products of E4M3 values are exact;
-    a 64-term float32 sum, the scale, one fused multiply-add) and of exp2.
+def rounding_slack(parts: dict, dot_rel_err: float = 2.0 ** -13, x_rel_err: float = 2.0 ** -20):
+    """Per-row bounds on what a streaming kernel may legitimately differ from
+    head_forward_fp8 by, through the two cases named in the module docstring:
+    (a) probabilities 2^(z - m) below 2^-13, whose codes depend on the
+    reference in use (each may move by at most 2^-17 after the final
+    rescale), and (b) codes whose argument x = 2^(z - m + 8) lies within the
+    kernel's error of x from a rounding midpoint (each may move by one grid
+    step). That error is taken as a dot-product error of at most
+    ``dot_rel_err`` * sum_c |Q^_ic K^_jc| (the sum of the magnitudes of the
+    exact products), which moves z by that / sqrt(d) * log2(e) and x by ln 2
+    times as much, relatively, plus ``x_rel_err`` for the scale, one fused
+    multiply-add and exp2 in float32.
 
     Returns (o_slack (T,), lse_slack (T,)): |dO_i| <= o_slack_i per channel
     and |dLSE_i| <= lse_slack_i, to first order in the moved weights.
     """
     z, m, p_hat, l = parts["z"], parts["m"], parts["p_hat"], parts["l"]
     v = parts["v"]
+    d = v.shape[1]
     o = (p_hat @ v) / l[:, None]
     x = np.exp2(z - m[:, None] + P_SHIFT)
     live = x > 0
@@ -275,7 +280,13 @@ def rounding_slack(parts: dict, z_rel: float = 2.0 ** -20):
     xs = np.where(live, np.minimum(x, E4M3_MAX), 1.0)
     lo, hi = _e4m3_neighbours(xs)
     mid = 0.5 * (lo + hi)
-    near = live & ~small & (np.abs(xs - mid) <= z_rel * xs)
+    dot_abs = np.abs(parts["q"]) @ np.abs(parts["k"]).T
+    rel = dot_rel_err * dot_abs / math.sqrt(d) + x_rel_err   # ln 2 * log2(e) = 1
+    if np.any(live & (rel > 2.0 ** -6)):
+        # A logit error that large can move a code by several grid steps and
+        # the row reference by more than one: the bound below would not hold.
+        raise ValueError("rounding_slack needs logit errors below 2^-6 (relative to x)")
+    near = live & ~small & (np.abs(xs - mid) <= rel * xs)
     move = move + np.where(near, (hi - lo) * 2.0 ** -P_SHIFT, 0.0)
     # |d(sum_j w_j v_j / sum_j w_j)| <= sum_j |dw_j| |v_j - O_i| / (l_i - sum_j |dw_j|)
     T = v.shape[0]

@@ -46,6 +46,7 @@ def test_header_declares_expected_entry_points():
               "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess", "attn_bwd_workspace_floats",
               "attn_fwd_unfused", "attn_bwd_unfused", "attn_unfused_workspace_bytes",
               "attn_decode", "attn_decode_workspace_floats",
+              "attn_fp8_buffer_bytes", "attn_quantize_fp8", "attn_fwd_fp8",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -181,6 +182,39 @@ def test_decode_workspace_size(L):
     assert L.attn_decode_workspace_floats(1, 1, 1) == 66            # one split: m, l, 64 sums
     assert L.attn_decode_workspace_floats(0, 5, 2) == 0
     assert L.attn_decode_workspace_floats(1, -1, 2) == -1
+
+
+@no_gpu_only
+def test_fp8_validation(L):
+    F8 = 0x70000000
+    fq, ff = L.attn_quantize_fp8, L.attn_fwd_fp8
+    ok = (1, 64, 2, 64)
+    assert fq(Q, None, *ok, None) == -1
+    assert fq(None, F8, *ok, None) == -1
+    assert fq(Q, F8, 1, 64, 2, 32, None) == -3                 # head_dim 32
+    assert fq(Q, F8 + 8, *ok, None) == -5
+    assert fq(Q, Q + 64, *ok, None) == -6                      # buffer inside qkv
+    assert fq(Q, F8, 1, 67108801, 1, 64, None) == -4           # round_up(T, 64) * 64 = 2^32
+    assert ff(None, O, LS, *ok, None) == -1
+    assert ff(F8, O, None, *ok, None) == -1
+    assert ff(F8, O + 8, LS, *ok, None) == -5
+    assert ff(F8, O, LS + 2, *ok, None) == -5
+    assert ff(F8, F8 + 128, LS, *ok, None) == -6               # out inside the buffer
+    assert ff(F8, O, O, *ok, None) == -6                       # lse is out
+    assert ff(F8, O, LS, 1, 64, 2, 32, None) == -3
+    for fn in (fq,):
+        assert fn(None, None, 0, 64, 2, 64, None) == 0
+    assert ff(None, None, None, 1, 0, 2, 64, None) == 0
+
+
+def test_fp8_buffer_size(L):
+    # 192 code bytes per (head, padded position) plus 384 exponent bytes per
+    # tile of 64 positions
+    assert L.attn_fp8_buffer_bytes(1, 64, 1) == 192 * 64 + 384
+    assert L.attn_fp8_buffer_bytes(1, 65, 2) == 2 * (192 * 128 + 2 * 384)
+    assert L.attn_fp8_buffer_bytes(16, 1024, 12) == 16 * 12 * (192 * 1024 + 16 * 384)
+    assert L.attn_fp8_buffer_bytes(0, 5, 2) == 0
+    assert L.attn_fp8_buffer_bytes(1, -1, 2) == -1
 
 
 def test_workspace_size(L):

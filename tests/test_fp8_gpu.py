@@ -1,0 +1,211 @@
+"""FP8 (MXFP8) attention forward against the CPU float64 FP8 oracle (needs a GPU).
+
+Quantization is integer work: every code and exponent byte of the FP8 buffer,
+padding included, must equal the oracle's bit for bit. The forward is
+compared per row with a bound made of the bf16 rounding of O (2^-8 relative),
+the accumulation error of the FP8 matrix product, and
+oracle.fp8.rounding_slack: what a streaming kernel may legitimately move
+(probabilities below 2^-13, and codes whose argument sits within the
+product's error of an E4M3 rounding midpoint).
+
+The scaled FP8 MFMA of gfx950 does not sum its 64 exact products in full
+float32: an in-bounds measurement over 2^21 outputs of random E4M3 operands
+found errors up to 2^-13.7 (median 2^-17.7) of the sum of the products'
+magnitudes, where the bf16 MFMA stays within 2^-23. The bound used here is
+2^-13 of that sum per product (ACC_EPS): on the logits through
+rounding_slack, and on O and LSE (whose sums run through the same MFMA) as
+2^-12 of max|V^| and 2^-12 absolute.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.fp8 as F
+from causal_flash_attention_amd import binding
+from causal_flash_attention_amd import inputs as I
+
+from helpers import log, sample_heads, to_device, to_host64
+
+pytestmark = pytest.mark.gpu
+
+D = 64
+ACC_EPS = 2.0 ** -13
+
+
+def _unpack(buf: np.ndarray, B: int, T: int, H: int):
+    """Split the FP8 buffer (uint8) into per-head arrays following the layout
+    documented in include/causal_attn.h."""
+    BH, Tp = B * H, (T + 63) // 64 * 64
+    NT = Tp // 64
+    n = BH * Tp * 64
+    assert buf.size >= 3 * n + BH * NT * 384
+    q = buf[:n].reshape(BH, Tp, 64)
+    k = buf[n:2 * n].reshape(BH, Tp, 64)
+    vt = buf[2 * n:3 * n].reshape(BH, 64, Tp)
+    ex = buf[3 * n:3 * n + BH * NT * 384].reshape(BH, NT, 384)
+    q_exp = ex[:, :, 0:128].reshape(BH, Tp, 2)
+    k_exp = ex[:, :, 128:256].reshape(BH, Tp, 2)
+    v_exp = ex[:, :, 256:384].reshape(BH, NT * 2, 64)
+    return q, k, vt, q_exp, k_exp, v_exp
+
+
+def _quantize(qkv_dev, B, T, H, fill=0xAB):
+    import torch
+    nbytes = binding.fp8_buffer_bytes(B, T, H)
+    buf = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+    binding.attn_quantize_fp8(qkv_dev, buf, H)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _check_quantization(host_buf, qkv64, B, T, H, heads):
+    q, k, vt, q_exp, k_exp, v_exp = _unpack(host_buf, B, T, H)
+    Tp = q.shape[1]
+    for b, h in heads:
+        bh = b * H + h
+        qq, kk, vv = oracle.split_packed_head(qkv64, b, h, H, D)
+        r = F.quantize_head(qq, kk, vv)
+        T32 = r["v_codes"].shape[0]
+        assert np.array_equal(q[bh, :T], r["q_codes"]), f"Q codes differ in head {b, h}"
+        assert np.array_equal(k[bh, :T], r["k_codes"]), f"K codes differ in head {b, h}"
+        assert np.array_equal(vt[bh].T[:T32], r["v_codes"]), f"V codes differ in head {b, h}"
+        assert np.array_equal(q_exp[bh, :T], r["q_exp"] + 127)
+        assert np.array_equal(k_exp[bh, :T], r["k_exp"] + 127)
+        assert np.array_equal(v_exp[bh, :T32 // 32], r["v_exp"] + 127)
+        # padding: zero codes, exponent byte 0
+        assert not q[bh, T:].any() and not k[bh, T:].any() and not vt[bh, :, T32:].any()
+        assert not q_exp[bh, T:].any() and not k_exp[bh, T:].any()
+        assert not v_exp[bh, T32 // 32:].any()
+
+
+def _check_forward(out, lse, qkv64, H, heads, tag):
+    """Per-row bound (rigorous given ACC_EPS) plus an aggregate gate: the
+    kernel-minus-oracle difference of O stays below 1% of O in relative L2, so
+    that borderline codes cannot hide a systematic error behind the bound."""
+    worst_o = worst_l = 0.0
+    slack_rows = 0
+    diff2 = ref2 = 0.0
+    for b, h in heads:
+        qq, kk, vv = oracle.split_packed_head(qkv64, b, h, H, D)
+        o_ref, l_ref, parts = F.head_forward_fp8(qq, kk, vv, return_parts=True)
+        o_slack, l_slack = F.rounding_slack(parts, dot_rel_err=ACC_EPS)
+        slack_rows += int((o_slack > 0).sum())
+        o = out[b, :, h * D:(h + 1) * D]
+        vmax = float(np.abs(parts["v"]).max())
+        base = 2.0 ** -8 * np.abs(o_ref) + 2 * ACC_EPS * vmax
+        o_bound = base + o_slack[:, None]
+        err = np.abs(o - o_ref)
+        bad = np.argwhere(err > o_bound)
+        assert len(bad) == 0, (f"{tag} head {b, h}: O off at rows/channels {bad[:5].tolist()}, "
+                               f"err {err[tuple(bad[0])]:.3e} bound {o_bound[tuple(bad[0])]:.3e}")
+        l_err = np.abs(lse[b, h] - l_ref)
+        l_bound = 2 * ACC_EPS + 2e-6 * np.abs(l_ref) + l_slack
+        assert np.all(l_err <= l_bound), f"{tag} head {b, h}: LSE off by {l_err.max():.3e}"
+        worst_o = max(worst_o, float((err / base).max()))
+        worst_l = max(worst_l, float(l_err.max()))
+        diff2 += float((err ** 2).sum())
+        ref2 += float((o_ref ** 2).sum())
+    rel = (diff2 / max(ref2, 1e-300)) ** 0.5
+    log(f"[parity] {tag}: O err / base bound <= {worst_o:.3f}, rel-L2 diff {rel:.2e}, "
+        f"LSE max-abs {worst_l:.3e}, rows with slack {slack_rows}")
+    assert rel <= 1e-2, f"{tag}: O differs from the oracle by {rel:.2e} relative L2"
+
+
+def _wide_range(B, T, H, seed, qk_top=12, v_top=12):
+    """Normal qkv times 2^k per element, k = floor(4 N(0, 1)) clipped to
+    [-12, qk_top] in Q and K and to [-12, v_top] in V (bf16): E4M3
+    subnormals and widely spread block scales."""
+    C = H * D
+    base = I.to_float64(I.attention_inputs(B, T, H, D, "bf16", 1.0, 1.0, seed=seed)[0], "bf16")
+    k = np.floor(I.to_float64(I.normal((B, T, 3 * C), 1.0, seed, 7, "f32"), "f32") * 4.0)
+    k[..., :2 * C] = np.clip(k[..., :2 * C], -12, qk_top)
+    k[..., 2 * C:] = np.clip(k[..., 2 * C:], -12, v_top)
+    x = base * np.exp2(k)
+    return I.f32_to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 63, 2), (1, 64, 1), (2, 65, 3), (1, 200, 2),
+                                   (2, 512, 2), (1, 1024, 2)])
+def test_fp8_quantize_bit_exact(B, T, H):
+    log(f"[case] fp8 quantize B={B} T={T} H={H}")
+    qkv, _ = I.attention_inputs(B, T, H, D, "bf16", 1.0, 1.0, seed=900 + T)
+    buf = _quantize(to_device(qkv, "bf16"), B, T, H)
+    _check_quantization(buf.cpu().numpy(), I.to_float64(qkv, "bf16"), B, T, H,
+                        [(b, h) for b in range(B) for h in range(H)])
+
+
+def test_fp8_quantize_wide_range():
+    B, T, H = 2, 200, 3
+    log(f"[case] fp8 quantize wide range B={B} T={T} H={H}")
+    qkv = _wide_range(B, T, H, seed=77)
+    buf = _quantize(to_device(qkv, "bf16"), B, T, H)
+    _check_quantization(buf.cpu().numpy(), I.to_float64(qkv, "bf16"), B, T, H,
+                        [(b, h) for b in range(B) for h in range(H)])
+
+
+@pytest.mark.parametrize("B,T,H,std", [(1, 1, 1, 1.0), (2, 63, 2, 1.0), (1, 64, 1, 1.0),
+                                       (2, 65, 3, 1.0), (1, 200, 2, 1.0), (2, 512, 2, 1.0),
+                                       (1, 1024, 2, 1.0), (1, 300, 2, 3.0), (2, 129, 1, 0.25)])
+def test_fp8_forward_parity(B, T, H, std):
+    import torch
+    log(f"[case] fp8 forward B={B} T={T} H={H} std={std}")
+    qkv, _ = I.attention_inputs(B, T, H, D, "bf16", std, 1.0, seed=1300 + T)
+    qkv_dev = to_device(qkv, "bf16")
+    out, lse = binding.forward_fp8(qkv_dev, H)
+    torch.cuda.synchronize()
+    qkv64 = I.to_float64(qkv, "bf16")
+    _check_forward(to_host64(out), to_host64(lse), qkv64, H,
+                   [(b, h) for b in range(B) for h in range(H)], f"B={B} T={T} H={H} std={std}")
+
+
+def test_fp8_forward_wide_range():
+    """Q and K spread over 2^-12 .. 2^2 (logits stay moderate, so the
+    accumulation error of the scores stays far below one grid step), V over
+    2^-12 .. 2^12."""
+    import torch
+    B, T, H = 1, 256, 2
+    log(f"[case] fp8 forward wide range B={B} T={T} H={H}")
+    qkv = _wide_range(B, T, H, seed=91, qk_top=2)
+    out, lse = binding.forward_fp8(to_device(qkv, "bf16"), H)
+    torch.cuda.synchronize()
+    _check_forward(to_host64(out), to_host64(lse), I.to_float64(qkv, "bf16"), H,
+                   [(0, 0), (0, 1)], "wide range")
+
+
+def test_fp8_headline_sampled():
+    """GPT-2 124M layer shape (B 16, T 1024, 12 heads): bit-exact quantization
+    and the forward bound on sampled heads, in the bench's launch shape."""
+    import torch
+    B, T, H = 16, 1024, 12
+    log(f"[case] fp8 headline B={B} T={T} H={H}")
+    qkv, _ = I.attention_inputs(B, T, H, D, "bf16", 1.0, 1.0, seed=2024)
+    qkv_dev = to_device(qkv, "bf16")
+    buf = _quantize(qkv_dev, B, T, H)
+    out = torch.empty((B, T, H * D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    binding.attn_fwd_fp8(buf, out, lse, H)
+    torch.cuda.synchronize()
+    heads = sample_heads(B, H, 6, seed=3)
+    qkv64 = I.to_float64(qkv, "bf16")
+    _check_quantization(buf.cpu().numpy(), qkv64, B, T, H, heads)
+    _check_forward(to_host64(out), to_host64(lse), qkv64, H, heads, "headline")
+
+
+def test_fp8_deterministic_and_close_to_exact():
+    """Two runs agree bit for bit; FP8 stays within a few percent (relative
+    L2) of exact attention on the unquantized inputs."""
+    import torch
+    B, T, H = 2, 384, 2
+    qkv, _ = I.attention_inputs(B, T, H, D, "bf16", 1.0, 1.0, seed=31)
+    qkv_dev = to_device(qkv, "bf16")
+    o1, l1 = binding.forward_fp8(qkv_dev, H)
+    o2, l2 = binding.forward_fp8(qkv_dev, H)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    ref, _ = oracle.forward_packed(I.to_float64(qkv, "bf16"), H, D)
+    o = to_host64(o1)
+    rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+    log(f"[accuracy] fp8 vs exact attention: rel-L2 {rel:.4f}")
+    assert rel < 0.08
