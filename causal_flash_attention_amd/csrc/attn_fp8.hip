@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256) void attn_quantize_fp8_kernel(const bf16* __re
 // ---------------------------------------------------------------------------
 constexpr int FWD_BM = 128;  // queries per workgroup (32 per wave)
 constexpr int FWD_BN = 64;   // keys per tile
-constexpr int NSTAGE = 3;
+// Tile j + 2 is issued during step j, into the stage that tile j - 1 has left.
+constexpr int PREFETCH = 2;
+constexpr int NSTAGE = PREFETCH + 1;
 
 struct Fp8Smem {
     u8 k[NSTAGE][64 * 64];  // K codes [key][channel], 16-byte chunks swizzled by swz_k
@@ -288,39 +290,15 @@ __device__ __forceinline__ i32x8 p_operand(const f32x16 (&x)[2]) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            int d = __builtin_amdgcn_cvt_pk_fp8_f32(x[kb][4 * w], x[kb][4 * w + 1], 0, false);
+            // Both halves of the word are written, so its old value does not
+            // matter: an empty asm output names a register without setting it.
+            int old;
+            asm volatile("" : "=v"(old));
+            int d = __builtin_amdgcn_cvt_pk_fp8_f32(x[kb][4 * w], x[kb][4 * w + 1], old, false);
             d = __builtin_amdgcn_cvt_pk_fp8_f32(x[kb][4 * w + 2], x[kb][4 * w + 3], d, true);
             r[4 * kb + w] = d;
         }
     return r;
-}
-
-enum NextTile { NEXT_NONE, NEXT_PLAIN, NEXT_MASKED };
-
-// One pipelined tile step: probabilities of tile j with the scores of tile
-// j + 1 on MFMA, then O^T += V^T P^T and l += 1^T P^T of tile j with the mask
-// and reference update of tile j + 1 on the VALU.
-template <int NEXT>
-__device__ __forceinline__ void step_f8(f32x16 (&s)[2], f32x16 (&s_next)[2], lds_u8* kt_next,
-                                        lds_u8* et_next, lds_u8* vt, lds_u8* et,
-                                        const F8Offsets& o, const i32x8& qop, int qs,
-                                        const i32x8& ones, f32x16 (&acc)[2], f32x16& lsum,
-                                        float& m_run, float c_log2, int lim_next) {
-    if (NEXT != NEXT_NONE) scores_f8(kt_next, et_next, o, qop, qs, s_next);
-    const float m8 = m_run - 8.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m8));
-    const i32x8 pop = p_operand(s);
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-        acc[db] = mfma_f8(lds_operand(vt, o.v[db]), pop, acc[db], et[o.ev[db]], P_SCALE);
-    lsum = mfma_f8(ones, pop, lsum, ONE_SCALE, P_SCALE);
-    if (NEXT != NEXT_NONE) {
-        if (NEXT == NEXT_MASKED) mask_f8(s_next, lim_next);
-        update_ref(tile_max_f8(s_next) * c_log2, m_run, acc, lsum);
-    }
 }
 
 __global__ __launch_bounds__(256, CATTN_FP8_WAVES_PER_SIMD) void attn_fwd_fp8_kernel(
@@ -375,8 +353,9 @@ __global__ __launch_bounds__(256, CATTN_FP8_WAVES_PER_SIMD) void attn_fwd_fp8_ke
         if (wave == 0 && lane < 16)
             lds_dma16_buf(rs_e, voff_e, (unsigned int)(j * F8_EXP_TILE + 128), lds_addr_u(sm.e[st]));
     };
-    issue(0, 0);
-    if (n_kt > 1) issue(1, 1);
+#pragma unroll
+    for (int j = 0; j < PREFETCH; ++j)
+        if (j < n_kt) issue(j, j);
 
     // Q^T operand (B of S^T): channels [16h, 16h + 16) and [32 + 16h, +16) of
     // this lane's query, with the exponent of channel block h.
@@ -398,39 +377,44 @@ __global__ __launch_bounds__(256, CATTN_FP8_WAVES_PER_SIMD) void attn_fwd_fp8_ke
     wait_vmem<0>();
     __syncthreads();
 
+    // One tile per step: scores, reference update, probabilities, then the
+    // P V and row-sum products. (Overlapping the scores of tile j + 1 with the
+    // exponentials of tile j needs 32 more registers per lane, which drops
+    // the kernel to two waves per SIMD and measured slower than three.)
     float m_run = -INFINITY;                 // integer reference of base-2 logits
     f32x16 acc[2] = {zero16(), zero16()};    // O^T per channel block
     f32x16 lsum = zero16();                  // row 0: sum of the probabilities
-    f32x16 s[2], s_next[2];
-    {
-        scores_f8(lds_view(sm.k[0]), lds_view(sm.e[0]), o, qop, qs, s);
-        if (j_last == 0) mask_f8(s, qw + l32 - 16 * hf);
-        update_ref(tile_max_f8(s) * c_log2, m_run, acc, lsum);
-    }
-
-    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-        wait_vmem<0>();
+    for (int j = 0; j < n_kt; ++j) {
+        // Tile j must have landed; the loads of tile j + 1 may stay in flight
+        // (each wave issues two per tile, wave 0 a third).
+        if (j >= 1 && j + 1 < n_kt) {
+            if (wave == 0) wait_vmem<3>();
+            else wait_vmem<2>();
+        } else {
+            wait_vmem<0>();
+        }
         __syncthreads();
-        if (j + 2 < n_kt) issue(j + 2, (j + 2) % NSTAGE);
-        if (j > j_last) return;
+        if (j + PREFETCH < n_kt) issue(j + PREFETCH, (j + PREFETCH) % NSTAGE);
+        if (j > j_last) continue;  // tiles above this wave's diagonal
+        lds_u8* kt = lds_view(sm.k[j % NSTAGE]);
         lds_u8* vt = lds_view(sm.v[j % NSTAGE]);
         lds_u8* et = lds_view(sm.e[j % NSTAGE]);
-        lds_u8* kt_next = lds_view(sm.k[(j + 1) % NSTAGE]);
-        lds_u8* et_next = lds_view(sm.e[(j + 1) % NSTAGE]);
-        const int lim_next = qw - (j + 1) * FWD_BN + l32 - 16 * hf;
-        if (j + 1 < j_last)
-            step_f8<NEXT_PLAIN>(cur, nxt, kt_next, et_next, vt, et, o, qop, qs, ones, acc, lsum,
-                                m_run, c_log2, lim_next);
-        else if (j + 1 == j_last)
-            step_f8<NEXT_MASKED>(cur, nxt, kt_next, et_next, vt, et, o, qop, qs, ones, acc, lsum,
-                                 m_run, c_log2, lim_next);
-        else
-            step_f8<NEXT_NONE>(cur, nxt, kt_next, et_next, vt, et, o, qop, qs, ones, acc, lsum,
-                               m_run, c_log2, lim_next);
-    };
-    for (int j = 0; j < n_kt; j += 2) {
-        step(j, s, s_next);
-        if (j + 1 < n_kt) step(j + 1, s_next, s);
+        f32x16 s[2];
+        scores_f8(kt, et, o, qop, qs, s);
+        const i32x8 va = lds_operand(vt, o.v[0]);
+        const i32x8 vb = lds_operand(vt, o.v[1]);
+        const int vsa = et[o.ev[0]], vsb = et[o.ev[1]];
+        if (j == j_last) mask_f8(s, qw - j * FWD_BN + l32 - 16 * hf);
+        update_ref(tile_max_f8(s) * c_log2, m_run, acc, lsum);
+        const float m8 = m_run - 8.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m8));
+        const i32x8 pop = p_operand(s);
+        acc[0] = mfma_f8(va, pop, acc[0], vsa, P_SCALE);
+        acc[1] = mfma_f8(vb, pop, acc[1], vsb, P_SCALE);
+        lsum = mfma_f8(ones, pop, lsum, ONE_SCALE, P_SCALE);
     }
 
     // O = acc / l (bf16), LSE = ln 2 (m + log2 l); row 0 of lsum lives in half 0.
