@@ -19,7 +19,9 @@ CPU oracle timed on a bounded sample of heads of the same workload;
 the T x T matrices through HBM) on the same inputs, after the timed region,
 and gives its ratio to the flash-attention step; ``decode`` times attn_decode
 over a K/V cache larger than the Infinity Cache and reports its HBM rate
-against the 8 TB/s roofline.
+against the 8 TB/s roofline; ``fp8`` times the FP8 forward (attn_quantize_fp8
+then attn_fwd_fp8) on the same qkv, against the FP8 MFMA peak, and reports
+how far its output lies from the bf16 forward's.
 """
 
 from __future__ import annotations
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "causal attention fwd+bwd TFLOP/s at GPT-2 124M shape; % of bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD specification
+FP8_PEAK_TFLOPS = 5033.2    # MI355X dense FP8 MFMA, AMD specification (twice bf16)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD specification
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "causal_flash_attention_amd", "csrc")
@@ -54,7 +57,9 @@ KERNELS = {
 }
 STAGES = list(KERNELS)
 # Kernels outside the step whose HBM traffic is also recorded: the decode pass.
-EXTRA_TRAFFIC = {"decode_partial": ("attn_decode_bf16.hip",)}
+EXTRA_TRAFFIC = {"decode_partial": ("attn_decode_bf16.hip",),
+                 "attn_quantize_fp8": ("attn_fp8.hip",),
+                 "attn_fwd_fp8": ("attn_fp8.hip",)}
 
 
 def parse_args(argv=None):
@@ -69,6 +74,7 @@ def parse_args(argv=None):
     p.add_argument("--no-unfused", action="store_true",
                    help="skip timing the materialising path")
     p.add_argument("--no-decode", action="store_true", help="skip timing decode")
+    p.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 forward")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -103,7 +109,7 @@ def traffic_from_profile(kernel: str, workload: str):
     m_val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     if not (m_src and m_val):
         return None
-    if m_src.group(1) != source_digest(os.path.join(CSRC, KERNELS[kernel][0])):
+    if m_src.group(1) != source_digest(os.path.join(CSRC, (KERNELS.get(kernel) or EXTRA_TRAFFIC[kernel])[0])):
         return None
     return float(m_val.group(1))
 
@@ -131,7 +137,9 @@ def _kernel_of(name: str):
     for k, tag in (("unfused_softmax_bwd", "softmax_bwd_rows_kernel"),
                    ("unfused_softmax", "softmax_rows_kernel"),
                    ("decode_partial", "decode_partial_kernel"),
-                   ("decode_combine", "decode_combine_kernel")):
+                   ("decode_combine", "decode_combine_kernel"),
+                   ("attn_fwd_fp8", "attn_fwd_fp8_kernel"),
+                   ("attn_quantize_fp8", "attn_quantize_fp8_kernel")):
         if tag in name:
             return k
     for k, tag in (("attn_fwd", "attn_fwd_bf16_kernel"), ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
@@ -151,7 +159,9 @@ def _counter_means(d: str, counter: str):
         k = _kernel_of(r.get("Kernel_Name", ""))
         if k:
             per.setdefault(k, []).append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in per.items()}
+    # The calibration is the 256 MiB copy, the largest runtime copy of the run
+    # (small runtime copies, such as a scalar staged for the host, also occur).
+    return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in per.items()}
 
 
 def write_profiles(args, w) -> int:
@@ -324,6 +334,64 @@ def time_decode(stream, calls=50):
                          "frac": gbs / HBM_PEAK_GBS}}
 
 
+def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, calls=100):
+    """The FP8 forward on the step's qkv: quantize and forward timed apart and
+    together; the forward's FLOP rate against the FP8 MFMA peak, the
+    quantization's HBM rate (bf16 qkv read, FP8 buffer written)."""
+    import torch
+
+    from causal_flash_attention_amd import binding
+
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    C = H * D
+    nbuf = binding.fp8_buffer_bytes(B, T, H)
+    buf = torch.empty(nbuf, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+
+    def quant():
+        binding.attn_quantize_fp8(qkv, buf, H, D, stream)
+
+    def fwd():
+        binding.attn_fwd_fp8(buf, out, lse, H, D, stream)
+
+    def both():
+        quant()
+        fwd()
+
+    def timed(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / calls
+
+    q_us, f_us, p_us = timed(quant), timed(fwd), timed(both)
+    fwd_flops = 2.0 * B * H * T * T * D  # S = QK^T and O = PV, causal halves counted
+    tf = fwd_flops / (f_us * 1e-6) / 1e12
+    qbytes = 3.0 * B * T * C * 2 + nbuf
+    gbs = qbytes / (q_us * 1e-6) / 1e9
+    ref = out_bf16.float()
+    rel = float(torch.linalg.vector_norm(out.float() - ref) / torch.linalg.vector_norm(ref))
+    return {"workload": w.name, "quantize_us": q_us, "fwd_us": f_us, "pass_us": p_us,
+            "calls": calls, "fwd_tflops": tf, "pass_tflops": fwd_flops / (p_us * 1e-6) / 1e12,
+            "fwd_speedup_vs_bf16_fwd": fwd_bf16_us / f_us,
+            "rel_l2_vs_bf16_fwd": rel,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / FP8_PEAK_TFLOPS,
+                         "traffic": traffic_from_profile("attn_fwd_fp8", w.name),
+                         "kernel": "attn_fwd_fp8"},
+            "quantize_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "bytes_per_call": qbytes,
+                                  "traffic": traffic_from_profile("attn_quantize_fp8", w.name)}}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -420,6 +488,13 @@ def main(argv=None):
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
     decode = None if args.no_decode else time_decode(stream)
+    if not args.no_fp8:
+        attn_fwd_out = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
+        attn_fwd_lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        binding.attn_fwd(qkv, attn_fwd_out, attn_fwd_lse, H, D, stream)
+        fp8 = time_fp8(w, qkv, attn_fwd_out, kernel_us["attn_fwd"], stream)
+    else:
+        fp8 = None
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -454,6 +529,8 @@ def main(argv=None):
         result["unfused"] = unfused
     if decode is not None:
         result["decode"] = decode
+    if fp8 is not None:
+        result["fp8"] = fp8
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
