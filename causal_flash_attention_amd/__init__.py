@@ -8,6 +8,8 @@ the library has not been built.
 
 from .binding import (  # noqa: F401
     AttnError,
+    attn_block_bwd,
+    attn_block_fwd,
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
@@ -23,6 +25,7 @@ from .binding import (  # noqa: F401
     attn_status_string,
     attn_version,
     backward,
+    block_workspace_bytes,
     decode_workspace_floats,
     forward,
     forward_fp8,

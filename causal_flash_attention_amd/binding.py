@@ -46,6 +46,9 @@ SIGNATURES = {
     "attn_decode": ([_P, ctypes.c_longlong, _P, _P, ctypes.c_longlong, ctypes.c_longlong,
                      _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_block_workspace_bytes": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_block_fwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_block_bwd": ([_P] * 15 + [_I, _I, _I, _I, _P], _I),
     "attn_fp8_buffer_bytes": ([_I, _I, _I], ctypes.c_longlong),
     "attn_quantize_fp8": ([_P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_fp8": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
@@ -310,6 +313,59 @@ def attn_decode(q, k_cache, v_cache, out, lse, ws, T: int, n_head: int, head_dim
     _check(lib().attn_decode(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache),
                              k_cache.stride(1), k_cache.stride(0), _ptr(out), _ptr(lse), _ptr(ws),
                              B, T, n_head, head_dim, _stream_ptr(stream)), "attn_decode")
+
+
+def block_workspace_bytes(B: int, T: int, n_head: int) -> int:
+    """Bytes of attn_block_bwd's workspace."""
+    n = int(lib().attn_block_workspace_bytes(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def attn_block_fwd(x, w_attn, b_attn, w_proj, b_proj, qkv, att, lse, y, n_head: int,
+                   head_dim: int = 64, stream=None) -> None:
+    torch = _torch()
+    if x is None or x.dim() != 3:
+        raise ValueError("x must be a (B, T, C) tensor")
+    B, T, C = (int(v) for v in x.shape)
+    if C != n_head * head_dim:
+        raise ValueError("x's last dimension must be n_head * head_dim")
+    bf = torch.bfloat16
+    for t, name, shape in ((x, "x", (B, T, C)), (w_attn, "w_attn", (C, 3 * C)),
+                           (b_attn, "b_attn", (3 * C,)), (w_proj, "w_proj", (C, C)),
+                           (b_proj, "b_proj", (C,)), (qkv, "qkv", (B, T, 3 * C)),
+                           (att, "att", (B, T, C)), (y, "y", (B, T, C))):
+        _require(t, name, bf, shape)
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _check(lib().attn_block_fwd(_ptr(x), _ptr(w_attn), _ptr(b_attn), _ptr(w_proj), _ptr(b_proj),
+                                _ptr(qkv), _ptr(att), _ptr(lse), _ptr(y), B, T, n_head, head_dim,
+                                _stream_ptr(stream)), "attn_block_fwd")
+
+
+def attn_block_bwd(dy, x, w_attn, w_proj, qkv, att, lse, datt, dqkv, dx, dw_attn, db_attn,
+                   dw_proj, db_proj, ws, n_head: int, head_dim: int = 64, stream=None) -> None:
+    torch = _torch()
+    if x is None or x.dim() != 3:
+        raise ValueError("x must be a (B, T, C) tensor")
+    B, T, C = (int(v) for v in x.shape)
+    if C != n_head * head_dim:
+        raise ValueError("x's last dimension must be n_head * head_dim")
+    bf, f32 = torch.bfloat16, torch.float32
+    for t, name, dt, shape in ((dy, "dy", bf, (B, T, C)), (x, "x", bf, (B, T, C)),
+                               (w_attn, "w_attn", bf, (C, 3 * C)), (w_proj, "w_proj", bf, (C, C)),
+                               (qkv, "qkv", bf, (B, T, 3 * C)), (att, "att", bf, (B, T, C)),
+                               (lse, "lse", f32, (B, n_head, T)), (datt, "datt", bf, (B, T, C)),
+                               (dqkv, "dqkv", bf, (B, T, 3 * C)), (dx, "dx", bf, (B, T, C)),
+                               (dw_attn, "dw_attn", f32, (C, 3 * C)), (db_attn, "db_attn", f32, (3 * C,)),
+                               (dw_proj, "dw_proj", f32, (C, C)), (db_proj, "db_proj", f32, (C,))):
+        _require(t, name, dt, shape)
+    _require_bytes(ws, "ws", block_workspace_bytes(B, T, n_head))
+    _check(lib().attn_block_bwd(_ptr(dy), _ptr(x), _ptr(w_attn), _ptr(w_proj), _ptr(qkv),
+                                _ptr(att), _ptr(lse), _ptr(datt), _ptr(dqkv), _ptr(dx),
+                                _ptr(dw_attn), _ptr(db_attn), _ptr(dw_proj), _ptr(db_proj),
+                                _ptr(ws), B, T, n_head, head_dim, _stream_ptr(stream)),
+           "attn_block_bwd")
 
 
 def fp8_buffer_bytes(B: int, T: int, n_head: int) -> int:

@@ -26,6 +26,14 @@ long long unfused_row_stride(int T);
 hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
                                        void*, int, int, int, hipStream_t);
 long long fp8_buffer_bytes(int B, int T, int H);
+long long block_workspace_floats(int B, int T, int H);
+hipError_t launch_attn_block_fwd_bf16(const void*, const void*, const void*, const void*,
+                                      const void*, void*, void*, float*, void*, int, int, int,
+                                      hipStream_t);
+hipError_t launch_attn_block_bwd_bf16(const void*, const void*, const void*, const void*,
+                                      const void*, const void*, const float*, void*, void*, void*,
+                                      float*, float*, float*, float*, float*, int, int, int,
+                                      hipStream_t);
 hipError_t launch_attn_quantize_fp8(const void*, void*, int, int, int, hipStream_t);
 hipError_t launch_attn_fwd_fp8(const void*, void*, float*, int, int, int, hipStream_t);
 hipError_t launch_attn_fwd_f32(const float*, float*, float*, int, int, int, hipStream_t);
@@ -262,6 +270,20 @@ int check_fp8(int T) {
     return ATTN_OK;
 }
 
+// Extra limit of the attention block: its column sums run one grid row per
+// 256 token rows.
+int check_block(int B, int T) {
+    if ((long long)B * T > 65535LL * 256)
+        return fail(ATTN_ERR_TOO_LARGE, "the attention block takes B*T <= 16776960");
+    return ATTN_OK;
+}
+
+int check_all_aligned(const void* const* ptrs, int n, uintptr_t a, const char* what) {
+    for (int i = 0; i < n; ++i)
+        if (reinterpret_cast<uintptr_t>(ptrs[i]) % a != 0) return fail(ATTN_ERR_MISALIGNED, what);
+    return ATTN_OK;
+}
+
 long long unfused_ws_bytes(int B, int T, int H) {
     return 6LL * B * H * T * cattn::unfused_row_stride(T);
 }
@@ -408,6 +430,82 @@ int attn_decode(const void* q, long long q_batch_stride, const void* k_cache, co
                                                         cache_row_stride, cache_batch_stride, out,
                                                         lse, ws, B, T, H, as_stream(stream));
     return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_decode launch");
+}
+
+long long attn_block_workspace_bytes(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    return 4 * cattn::block_workspace_floats(B, T, n_head);
+}
+
+int attn_block_fwd(const void* x, const void* w_attn, const void* b_attn, const void* w_proj,
+                   const void* b_proj, void* qkv, void* att, float* lse, void* y, int B, int T,
+                   int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) &&
+        (!x || !w_attn || !b_attn || !w_proj || !b_proj || !qkv || !att || !lse || !y))
+        return fail(ATTN_ERR_NULL_PTR, "attn_block_fwd: an argument pointer is NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_block(B, T)) != ATTN_OK) return st;
+    const void* al16[] = {x, w_attn, w_proj, qkv, att, y};
+    if ((st = check_all_aligned(al16, 6, 16, "x, weights, qkv, att and y must be 16-byte aligned")) != ATTN_OK)
+        return st;
+    const void* al2[] = {b_attn, b_proj};
+    if ((st = check_all_aligned(al2, 2, 2, "biases must be 2-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const long long C = (long long)H * head_dim;
+    const Span ins[] = {span(x, z.bt_c, "x"), span(w_attn, C * 3 * C * 2, "w_attn"),
+                        span(b_attn, 3 * C * 2, "b_attn"), span(w_proj, C * C * 2, "w_proj"),
+                        span(b_proj, C * 2, "b_proj")};
+    const Span outs[] = {span(qkv, z.qkv, "qkv"), span(att, z.bt_c, "att"), span(lse, z.rows, "lse"),
+                         span(y, z.bt_c, "y")};
+    if ((st = check_disjoint(outs, 4, ins, 5)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_block_fwd_bf16(x, w_attn, b_attn, w_proj, b_proj, qkv,
+                                                           att, lse, y, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_block_fwd launch");
+}
+
+int attn_block_bwd(const void* dy, const void* x, const void* w_attn, const void* w_proj,
+                   const void* qkv, const void* att, const float* lse, void* datt, void* dqkv,
+                   void* dx, float* dw_attn, float* db_attn, float* dw_proj, float* db_proj,
+                   float* ws, int B, int T, int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) &&
+        (!dy || !x || !w_attn || !w_proj || !qkv || !att || !lse || !datt || !dqkv || !dx ||
+         !dw_attn || !db_attn || !dw_proj || !db_proj || !ws))
+        return fail(ATTN_ERR_NULL_PTR, "attn_block_bwd: an argument pointer is NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_block(B, T)) != ATTN_OK) return st;
+    const void* al16[] = {dy, x, w_attn, w_proj, qkv, att, datt, dqkv, dx, ws};
+    if ((st = check_all_aligned(al16, 10, 16,
+                                "matrices, weights and ws must be 16-byte aligned")) != ATTN_OK)
+        return st;
+    const void* al4[] = {lse, dw_attn, db_attn, dw_proj, db_proj};
+    if ((st = check_all_aligned(al4, 5, 4, "lse and the float32 gradients must be 4-byte aligned")) !=
+        ATTN_OK)
+        return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const long long C = (long long)H * head_dim;
+    const Span ins[] = {span(dy, z.bt_c, "dy"), span(x, z.bt_c, "x"),
+                        span(w_attn, C * 3 * C * 2, "w_attn"), span(w_proj, C * C * 2, "w_proj"),
+                        span(qkv, z.qkv, "qkv"), span(att, z.bt_c, "att"), span(lse, z.rows, "lse")};
+    const Span outs[] = {span(datt, z.bt_c, "datt"), span(dqkv, z.qkv, "dqkv"),
+                         span(dx, z.bt_c, "dx"), span(dw_attn, C * 3 * C * 4, "dw_attn"),
+                         span(db_attn, 3 * C * 4, "db_attn"), span(dw_proj, C * C * 4, "dw_proj"),
+                         span(db_proj, C * 4, "db_proj"),
+                         span(ws, 4 * cattn::block_workspace_floats(B, T, H), "ws")};
+    if ((st = check_disjoint(outs, 8, ins, 7)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_block_bwd_bf16(
+        dy, x, w_attn, w_proj, qkv, att, lse, datt, dqkv, dx, dw_attn, db_attn, dw_proj, db_proj,
+        ws, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_block_bwd launch");
 }
 
 long long attn_fp8_buffer_bytes(int B, int T, int n_head) {

@@ -1,0 +1,165 @@
+// The attention layer around the fused attention, bf16 storage, fp32
+// accumulation (gfx950): c_attn, causal attention, c_proj, forward and
+// backward ("Let's reproduce GPT-2 (124M)", chapter list, 00:13:47 for the
+// layer; 01:48:15 kernel fusion and 02:00:18 flash attention for making it
+// fast).
+//
+//   forward:  qkv = x W_attn + b_attn;  att, lse = attention(qkv);
+//             y = att W_proj + b_proj
+//   backward: datt = dy W_proj^T;  dW_proj = att^T dy;  db_proj = colsum(dy);
+//             dqkv = attention backward(datt);  dx = dqkv W_attn^T;
+//             dW_attn = x^T dqkv;  db_attn = colsum(dqkv)
+//
+// The neighbours meet the attention in its own layouts, so nothing is
+// reshaped, transposed or copied between them: the c_attn product's epilogue
+// adds the bias and writes the packed [Q | K | V] rows the attention kernels
+// read, and the c_proj product reads the attention's (B, T, C) output as its
+// A operand in place (and datt, its gradient, in the layout the backward
+// reads as dO). Weights are stored (in, out).
+//
+// The weight gradients are long contractions (K = B * T) with small outputs,
+// so they run split over K into fp32 slabs that a second kernel adds in a
+// fixed order; the bias gradients are column sums done the same way. No
+// atomics: the backward is deterministic.
+#include "attn_common.h"
+
+namespace cattn {
+
+hipError_t launch_gemm_bf16(bool a_tr, bool b_tr, bool out_f32, const void* A, long long lda,
+                            const void* B, long long ldb, void* C, long long ldc, const void* bias,
+                            int M, int N, int K, int splits, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const void*, void*, float*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
+                                       void*, int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, void*, int, int, int,
+                                     hipStream_t);
+
+namespace {
+
+constexpr int COLSUM_ROWS = 256;  // rows per partial column sum
+
+// parts[s * N + n] = sum of X[r, n] over rows r of chunk s (COLSUM_ROWS rows),
+// in row order. One thread per column; grid (ceil(N / 256), chunks).
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const bf16* __restrict__ X,
+                                                             long long ld, int R, int N,
+                                                             float* __restrict__ parts) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    const int r0 = blockIdx.y * COLSUM_ROWS, r1 = min(R, r0 + COLSUM_ROWS);
+    float acc = 0.0f;
+    for (int r = r0; r < r1; ++r) acc += (float)X[(long long)r * ld + n];
+    parts[(long long)blockIdx.y * N + n] = acc;
+}
+
+// out[i] = sum over s = 0 .. S-1 of parts[s * n + i], in that order.
+__global__ __launch_bounds__(256) void sum_slabs_kernel(const float* __restrict__ parts, int S,
+                                                        long long n, float* __restrict__ out) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.0f;
+    for (int s = 0; s < S; ++s) acc += parts[(long long)s * n + i];
+    out[i] = acc;
+}
+
+hipError_t colsum(const bf16* X, long long ld, int R, int N, float* parts, float* out,
+                  hipStream_t stream) {
+    const int chunks = (R + COLSUM_ROWS - 1) / COLSUM_ROWS;
+    hipLaunchKernelGGL(colsum_partial_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)chunks),
+                       dim3(256), 0, stream, X, ld, R, N, parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                       parts, chunks, (long long)N, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// K splits of a weight-gradient product over R = B * T rows: as many as keep
+// about 1024 workgroups busy for an M x N output of 128 x 128 tiles, each
+// split a whole number of 64-row steps (1 when R is not a multiple of 64).
+int block_splits(long long R, int M, int N) {
+    const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    int s = 1;
+    while (s < 64 && tiles * s * 2 <= 1024 && R % (64LL * s * 2) == 0) s *= 2;
+    return s;
+}
+
+long long block_workspace_floats(int B, int T, int H) {
+    const long long C = (long long)H * HEAD_DIM, R = (long long)B * T;
+    const long long tp = ((long long)T + 63) / 64 * 64;
+    const long long delta = 10LL * B * H * tp;
+    const long long s_attn = block_splits(R, (int)C, (int)(3 * C));
+    const long long s_proj = block_splits(R, (int)C, (int)C);
+    long long parts = s_attn * C * 3 * C;
+    if (s_proj * C * C > parts) parts = s_proj * C * C;
+    const long long cs = (R + COLSUM_ROWS - 1) / COLSUM_ROWS * 3 * C;
+    if (cs > parts) parts = cs;
+    return delta + parts;
+}
+
+hipError_t launch_attn_block_fwd_bf16(const void* x, const void* w_attn, const void* b_attn,
+                                      const void* w_proj, const void* b_proj, void* qkv, void* att,
+                                      float* lse, void* y, int B, int T, int H,
+                                      hipStream_t stream) {
+    const long long C = (long long)H * HEAD_DIM;
+    const int R = B * T;
+    hipError_t e = launch_gemm_bf16(false, true, false, x, C, w_attn, 3 * C, qkv, 3 * C, b_attn, R,
+                                    (int)(3 * C), (int)C, 1, stream);
+    if (e != hipSuccess) return e;
+    if ((e = launch_attn_fwd_bf16(qkv, att, lse, B, T, H, stream)) != hipSuccess) return e;
+    return launch_gemm_bf16(false, true, false, att, C, w_proj, C, y, C, b_proj, R, (int)C,
+                            (int)C, 1, stream);
+}
+
+hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void* w_attn,
+                                      const void* w_proj, const void* qkv, const void* att,
+                                      const float* lse, void* datt, void* dqkv, void* dx,
+                                      float* dw_attn, float* db_attn, float* dw_proj,
+                                      float* db_proj, float* ws, int B, int T, int H,
+                                      hipStream_t stream) {
+    const long long C = (long long)H * HEAD_DIM;
+    const int R = B * T;
+    const long long tp = ((long long)T + 63) / 64 * 64;
+    float* delta = ws;
+    float* parts = ws + 10LL * B * H * tp;
+    // c_proj backward
+    hipError_t e = launch_gemm_bf16(false, false, false, dy, C, w_proj, C, datt, C, nullptr, R,
+                                    (int)C, (int)C, 1, stream);
+    if (e != hipSuccess) return e;
+    const int sp = block_splits(R, (int)C, (int)C);
+    if ((e = launch_gemm_bf16(true, true, true, att, C, dy, C, sp > 1 ? parts : dw_proj, C,
+                              nullptr, (int)C, (int)C, R / sp, sp, stream)) != hipSuccess)
+        return e;
+    if (sp > 1) {
+        hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((C * C + 255) / 256)), dim3(256), 0,
+                           stream, parts, sp, C * C, dw_proj);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = colsum(static_cast<const bf16*>(dy), C, R, (int)C, parts, db_proj, stream)) !=
+        hipSuccess)
+        return e;
+    // attention backward: dqkv from datt (the dO of the attention)
+    if ((e = launch_attn_bwd_dq_pre_bf16(qkv, datt, att, lse, delta, dqkv, B, T, H, stream)) !=
+        hipSuccess)
+        return e;
+    if ((e = launch_attn_bwd_dkdv_bf16(qkv, datt, delta, dqkv, B, T, H, stream)) != hipSuccess)
+        return e;
+    // c_attn backward
+    if ((e = launch_gemm_bf16(false, false, false, dqkv, 3 * C, w_attn, 3 * C, dx, C, nullptr, R,
+                              (int)C, (int)(3 * C), 1, stream)) != hipSuccess)
+        return e;
+    const int sa = block_splits(R, (int)C, (int)(3 * C));
+    if ((e = launch_gemm_bf16(true, true, true, x, C, dqkv, 3 * C, sa > 1 ? parts : dw_attn,
+                              3 * C, nullptr, (int)C, (int)(3 * C), R / sa, sa, stream)) !=
+        hipSuccess)
+        return e;
+    if (sa > 1) {
+        hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((C * 3 * C + 255) / 256)), dim3(256),
+                           0, stream, parts, sa, C * 3 * C, dw_attn);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return colsum(static_cast<const bf16*>(dqkv), 3 * C, R, (int)(3 * C), parts, db_attn, stream);
+}
+
+}  // namespace cattn

@@ -47,6 +47,7 @@ struct Operand {
 struct Output {
     void* base;  // float or bf16 elements
     long long stride_b, stride_h, ld;
+    const bf16* bias;  // added to every row (bias[n] for column n) when not null
 };
 
 struct GemmShape {
@@ -169,12 +170,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
         for (int nb = 0; nb < 2; ++nb) {
             const int n = n0 + wn0 + nb * 32 + l32;
             if (n >= g.N) continue;
+            const float bias = Cout.bias ? (float)Cout.bias[n] : 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int m = m0 + wm0 + mb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
                 if (m >= g.M) continue;
                 const long long off = b * Cout.stride_b + h * Cout.stride_h + (long long)m * Cout.ld + n;
-                const float v = g.alpha * acc[mb][nb][i];
+                const float v = g.alpha * acc[mb][nb][i] + bias;
                 if (OUT_F32) static_cast<float*>(Cout.base)[off] = v;
                 else static_cast<bf16*>(Cout.base)[off] = (bf16)v;
             }
@@ -314,6 +316,29 @@ hipError_t gemm(Operand A, Operand B, Output C, int M, int N, int K, int BH, int
 }
 
 }  // namespace
+
+// One plain (un-batched) product C = A B (+ bias per column) for the linear
+// maps around the attention, or `splits` independent products over
+// consecutive K ranges (split_k elements each) into consecutive M x N fp32
+// slabs. A is M x K, stored k-contiguous (a_tr false, row stride lda) or
+// m-contiguous (a_tr true: element (m, k) at k * lda + m); B is K x N, stored
+// n-contiguous (b_tr true: element (k, n) at k * ldb + n) or k-contiguous
+// (b_tr false: element (k, n) at n * ldb + k). C has row stride ldc.
+hipError_t launch_gemm_bf16(bool a_tr, bool b_tr, bool out_f32, const void* A_v, long long lda,
+                            const void* B_v, long long ldb, void* C_v, long long ldc,
+                            const void* bias, int M, int N, int K, int splits,
+                            hipStream_t stream) {
+    const bf16* A_p = static_cast<const bf16*>(A_v);
+    const bf16* B_p = static_cast<const bf16*>(B_v);
+    // a K chunk of split k starts K * k elements along k
+    const long long a_step = a_tr ? (long long)K * lda : K, b_step = b_tr ? (long long)K * ldb : K;
+    const Operand A{A_p, 0, a_step, lda}, B{B_p, 0, b_step, ldb};
+    const Output C{C_v, 0, (long long)M * ldc, ldc, static_cast<const bf16*>(bias)};
+    if (!a_tr && b_tr && !out_f32) return gemm<OP_ROW, OP_TR, 128, false>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
+    if (!a_tr && !b_tr && !out_f32) return gemm<OP_ROW, OP_ROW, 128, false>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
+    if (a_tr && b_tr && out_f32) return gemm<OP_TR, OP_TR, 128, true>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
+    return hipErrorInvalidValue;  // orientation not used by the library
+}
 
 int unfused_max_T() { return 4096; }  // Tp8 <= 4096 columns fit one wave's registers
 

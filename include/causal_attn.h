@@ -194,6 +194,40 @@ int attn_decode(const void* q, long long q_batch_stride,
                 void* out, float* lse, float* ws,
                 int B, int T, int n_head, int head_dim, void* stream);
 
+/* ------------------------------------------------- attention block (bf16) ---- */
+
+/* The attention layer of GPT-2 around the fused attention ("Let's reproduce
+ * GPT-2 (124M)", chapter list, 00:13:47 for the layer, 01:48:15 and 02:00:18
+ * for fusing and flash attention): with x (B, T, C), weights stored (in, out)
+ * and C = n_head * head_dim,
+ *   attn_block_fwd: qkv = x W_attn + b_attn (the packed layout of attn_fwd,
+ *     bias added in the product's epilogue); att, lse = attn_fwd(qkv);
+ *     y = att W_proj + b_proj (att read in place as the product's operand).
+ *   attn_block_bwd: datt = dy W_proj^T; dW_proj = att^T dy;
+ *     db_proj = sum over rows of dy; dqkv = attn_bwd(datt, qkv, att, lse);
+ *     dx = dqkv W_attn^T; dW_attn = x^T dqkv; db_attn = sum over rows of dqkv.
+ * bf16, row-major: x, y, att, dy, datt, dx (B, T, C); qkv, dqkv (B, T, 3C);
+ * w_attn (C, 3C); w_proj (C, C); b_attn (3C); b_proj (C). float32: lse
+ * (B, n_head, T); dw_attn (C, 3C), db_attn (3C), dw_proj (C, C), db_proj (C),
+ * overwritten. qkv, att and lse must come from attn_block_fwd on the same x
+ * and weights; datt and dqkv are written by attn_block_bwd (the gradients
+ * the layer passes through). ws: caller-owned float32 workspace of
+ * attn_block_workspace_bytes(B, T, n_head) bytes (the attention backward's
+ * delta, then K-split partial sums of the weight and bias gradients, added
+ * in a fixed order: the result does not depend on anything but the inputs).
+ * All launches go on `stream`; nothing is allocated. Matrices, weights and ws
+ * must be 16-byte aligned, biases 2-byte, float32 gradients and lse 4-byte;
+ * no output may overlap an input or another output. Extra limit:
+ * B * T <= 16776960 (ATTN_ERR_TOO_LARGE). */
+long long attn_block_workspace_bytes(int B, int T, int n_head);
+int attn_block_fwd(const void* x, const void* w_attn, const void* b_attn, const void* w_proj,
+                   const void* b_proj, void* qkv, void* att, float* lse, void* y, int B, int T,
+                   int n_head, int head_dim, void* stream);
+int attn_block_bwd(const void* dy, const void* x, const void* w_attn, const void* w_proj,
+                   const void* qkv, const void* att, const float* lse, void* datt, void* dqkv,
+                   void* dx, float* dw_attn, float* db_attn, float* dw_proj, float* db_proj,
+                   float* ws, int B, int T, int n_head, int head_dim, void* stream);
+
 /* ------------------------------------------------------------ FP8 (MXFP8) ---- */
 
 /* Causal attention forward with FP8 operands. The llm.c page ("Réimplémenter

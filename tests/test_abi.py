@@ -47,6 +47,7 @@ def test_header_declares_expected_entry_points():
               "attn_fwd_unfused", "attn_bwd_unfused", "attn_unfused_workspace_bytes",
               "attn_decode", "attn_decode_workspace_floats",
               "attn_fp8_buffer_bytes", "attn_quantize_fp8", "attn_fwd_fp8",
+              "attn_block_fwd", "attn_block_bwd", "attn_block_workspace_bytes",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -205,6 +206,49 @@ def test_fp8_validation(L):
     for fn in (fq,):
         assert fn(None, None, 0, 64, 2, 64, None) == 0
     assert ff(None, None, None, 1, 0, 2, 64, None) == 0
+
+
+@no_gpu_only
+def test_block_validation(L):
+    X, WA, BA, WP, BP = 0x70000000, 0x71000000, 0x72000000, 0x73000000, 0x74000000
+    QK, AT, LSE, Y = 0x80000000, 0x81000000, 0x82000000, 0x83000000
+    f = L.attn_block_fwd
+    ok = (2, 64, 2, 64)
+    assert f(X, WA, BA, WP, BP, QK, AT, LSE, None, *ok, None) == -1
+    assert f(X, WA, BA, WP, BP, QK, AT, LSE, Y, 2, 64, 2, 32, None) == -3
+    assert f(X + 8, WA, BA, WP, BP, QK, AT, LSE, Y, *ok, None) == -5
+    assert f(X, WA, BA + 1, WP, BP, QK, AT, LSE, Y, *ok, None) == -5
+    assert f(X, WA, BA, WP, BP, X + 64, AT, LSE, Y, *ok, None) == -6     # qkv inside x
+    assert f(X, WA, BA, WP, BP, QK, AT, LSE, QK + 128, *ok, None) == -6  # y inside qkv
+    assert f(X, WA, BA, WP, BP, QK, AT, LSE, Y, 65536, 256, 1, 64, None) == -4  # B*T too large
+    assert f(None, None, None, None, None, None, None, None, None, 0, 64, 2, 64, None) == 0
+    g = L.attn_block_bwd
+    D8 = [0x90000000 + i * 0x1000000 for i in range(8)]       # datt .. ws
+    args = [0x60000000, X, WA, WP, QK, AT, LSE] + D8
+    assert g(*args, *ok, None) != -1
+    bad = list(args)
+    bad[14] = None                                            # ws
+    assert g(*bad, *ok, None) == -1
+    bad = list(args)
+    bad[7] = D8[0] + 8                                        # datt misaligned
+    assert g(*bad, *ok, None) == -5
+    bad = list(args)
+    bad[9] = args[0] + 64                                     # dx inside dy
+    assert g(*bad, *ok, None) == -6
+    bad = list(args)
+    bad[11] = D8[3] + 8                                       # db_attn inside dw_attn
+    assert g(*bad, *ok, None) == -6
+
+
+def test_block_workspace_size(L):
+    # delta (10 floats per padded row) plus the largest of the K-split
+    # partials of dW_attn and dW_proj and the column-sum partials
+    n = L.attn_block_workspace_bytes(16, 1024, 12)
+    assert n >= 4 * (10 * 16 * 12 * 1024 + 768 * 2304)
+    assert n % 4 == 0
+    assert L.attn_block_workspace_bytes(1, 1, 1) >= 4 * (10 * 64 + 64 * 192)
+    assert L.attn_block_workspace_bytes(0, 5, 2) == 0
+    assert L.attn_block_workspace_bytes(1, -1, 2) == -1
 
 
 def test_fp8_buffer_size(L):
