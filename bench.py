@@ -19,7 +19,9 @@ CPU oracle timed on a bounded sample of heads of the same workload;
 the T x T matrices through HBM) on the same inputs, after the timed region,
 and gives its ratio to the flash-attention step; ``decode`` times attn_decode
 over a K/V cache larger than the Infinity Cache and reports its HBM rate
-against the 8 TB/s roofline; ``fp8`` times the FP8 forward (attn_quantize_fp8
+against the 8 TB/s roofline; ``block`` times the whole attention layer
+(attn_block_fwd + attn_block_bwd: c_attn, attention, c_proj and their
+gradients) at the same shape; ``fp8`` times the FP8 forward (attn_quantize_fp8
 then attn_fwd_fp8) on the same qkv, against the FP8 MFMA peak, and reports
 how far its output lies from the bf16 forward's.
 """
@@ -75,6 +77,7 @@ def parse_args(argv=None):
                    help="skip timing the materialising path")
     p.add_argument("--no-decode", action="store_true", help="skip timing decode")
     p.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 forward")
+    p.add_argument("--no-block", action="store_true", help="skip timing the attention layer")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -134,7 +137,9 @@ def _kernel_of(name: str):
     if m:  # materialising path: operand orientations, output tile width, output type
         ori = "".join("r" if x == "0" else "t" for x in m.group(1, 2))
         return f"unfused_gemm_{ori}{m.group(3)}_{'f32' if m.group(4) == 'true' else 'bf16'}"
-    for k, tag in (("unfused_softmax_bwd", "softmax_bwd_rows_kernel"),
+    for k, tag in (("block_colsum", "colsum_partial_kernel"),
+                   ("block_sum_slabs", "sum_slabs_kernel"),
+                   ("unfused_softmax_bwd", "softmax_bwd_rows_kernel"),
                    ("unfused_softmax", "softmax_rows_kernel"),
                    ("decode_partial", "decode_partial_kernel"),
                    ("decode_combine", "decode_combine_kernel"),
@@ -334,6 +339,71 @@ def time_decode(stream, calls=50):
                          "frac": gbs / HBM_PEAK_GBS}}
 
 
+def time_block(w, attn_step_us, stream, calls=50):
+    """The attention layer around the fused attention, forward + backward,
+    GPT-2 initialisation scale (weights and biases N(0, 0.02^2)), seeded."""
+    import torch
+
+    from causal_flash_attention_amd import binding
+
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    C = H * D
+    bf, dev = torch.bfloat16, "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    rnd = lambda *s, std=1.0: (torch.randn(s, generator=g, device=dev, dtype=torch.float32) * std).to(bf)  # noqa: E731
+    x, dy = rnd(B, T, C), rnd(B, T, C)
+    wa, ba, wp, bp = rnd(C, 3 * C, std=0.02), rnd(3 * C, std=0.02), rnd(C, C, std=0.02), rnd(C, std=0.02)
+    qkv = torch.empty((B, T, 3 * C), dtype=bf, device=dev)
+    att = torch.empty((B, T, C), dtype=bf, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    y = torch.empty((B, T, C), dtype=bf, device=dev)
+    datt, dx = torch.empty_like(att), torch.empty_like(att)
+    dqkv = torch.empty_like(qkv)
+    dwa, dba = torch.empty((C, 3 * C), device=dev), torch.empty(3 * C, device=dev)
+    dwp, dbp = torch.empty((C, C), device=dev), torch.empty(C, device=dev)
+    ws = torch.empty(binding.block_workspace_bytes(B, T, H), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        binding.attn_block_fwd(x, wa, ba, wp, bp, qkv, att, lse, y, H, D, stream)
+
+    def bwd():
+        binding.attn_block_bwd(dy, x, wa, wp, qkv, att, lse, datt, dqkv, dx, dwa, dba, dwp, dbp,
+                               ws, H, D, stream)
+
+    for _ in range(20):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(calls):
+        ev[0].record(stream)
+        fwd()
+        ev[1].record(stream)
+        bwd()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        f_ms += ev[0].elapsed_time(ev[1])
+        b_ms += ev[1].elapsed_time(ev[2])
+    f_us, b_us = 1000.0 * f_ms / calls, 1000.0 * b_ms / calls
+    R = B * T
+    lin = 2.0 * R * C * 3 * C + 2.0 * R * C * C     # c_attn + c_proj, forward
+    attn = w.counted_flops()["total"]
+    total = 3.0 * lin + attn                         # backward: data and weight gradients
+    step_us = f_us + b_us
+    lin_us = max(step_us - attn_step_us, 1e-3)       # linear maps and gradient sums
+    lin_tf = 3.0 * lin / (lin_us * 1e-6) / 1e12
+    return {"workload": f"{w.name} attention layer (c_attn, attention, c_proj), weights N(0, 0.02^2)",
+            "fwd_us": f_us, "bwd_us": b_us, "step_us": step_us, "calls": calls,
+            "counted_gflop": total / 1e9, "tflops": total / (step_us * 1e-6) / 1e12,
+            "linear_us": lin_us, "linear_tflops": lin_tf,
+            "linear_roofline": {"bound": "mfma", "achieved": lin_tf, "peak": BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": lin_tf / BF16_PEAK_TFLOPS,
+                                "what": "the six products of c_attn and c_proj (forward, data and "
+                                        "weight gradients) with the bias sums, timed as the layer "
+                                        "step minus the attention step"}}
+
+
 def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, calls=100):
     """The FP8 forward on the step's qkv: quantize and forward timed apart and
     together; the forward's FLOP rate against the FP8 MFMA peak, the
@@ -488,6 +558,7 @@ def main(argv=None):
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
     decode = None if args.no_decode else time_decode(stream)
+    block = None if args.no_block else time_block(w, ms_per_step * 1000.0, stream)
     if not args.no_fp8:
         attn_fwd_out = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
         attn_fwd_lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
@@ -531,6 +602,8 @@ def main(argv=None):
         result["decode"] = decode
     if fp8 is not None:
         result["fp8"] = fp8
+    if block is not None:
+        result["block"] = block
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

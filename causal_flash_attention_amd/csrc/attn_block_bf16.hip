@@ -37,18 +37,56 @@ hipError_t launch_attn_bwd_dkdv_bf16(const void*, const void*, const float*, voi
 namespace {
 
 constexpr int COLSUM_ROWS = 256;  // rows per partial column sum
+constexpr int COLSUM_COLS = 512;  // columns per workgroup (64 threads x 8)
 
-// parts[s * N + n] = sum of X[r, n] over rows r of chunk s (COLSUM_ROWS rows),
-// in row order. One thread per column; grid (ceil(N / 256), chunks).
+// parts[s * N + n] = sum of X[r, n] over the COLSUM_ROWS rows r of chunk s.
+// Workgroup (column block, chunk s): thread t owns columns 8 (t % 64) .. +7
+// of the block (16-byte loads) and rows 64 (t / 64) .. +63 of the chunk,
+// summed in row order; the four row groups are then added in group order
+// through LDS. N must be a multiple of 8 and X's rows 16-byte aligned.
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const bf16* __restrict__ X,
                                                              long long ld, int R, int N,
                                                              float* __restrict__ parts) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    const int r0 = blockIdx.y * COLSUM_ROWS, r1 = min(R, r0 + COLSUM_ROWS);
+    __shared__ float red[4][64][9];
+    const int t = threadIdx.x, col8 = t & 63, grp = t >> 6;
+    const int n0 = blockIdx.x * COLSUM_COLS + 8 * col8;
+    const int r0 = blockIdx.y * COLSUM_ROWS + 64 * grp;
+    const int r1 = min(R, r0 + 64);
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (n0 < N) {
+        const bf16* p = X + (long long)r0 * ld + n0;
+#pragma unroll 8
+        for (int r = r0; r < r1; ++r, p += ld) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[grp][col8][e] = acc[e];
+    __syncthreads();
+    if (grp == 0 && n0 < N) {
+        float* out = parts + (long long)blockIdx.y * N + n0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            out[e] = ((red[0][col8][e] + red[1][col8][e]) + red[2][col8][e]) + red[3][col8][e];
+    }
+}
+
+// out[n] = sum over chunks of parts[s * N + n]: thread (column, group) sums
+// the chunks s = group, group + 4, ... in order, then the four groups are
+// added in group order.
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ parts,
+                                                           int S, int N, float* __restrict__ out) {
+    __shared__ float red[4][64];
+    const int t = threadIdx.x, c = t & 63, grp = t >> 6;
+    const int n = blockIdx.x * 64 + c;
     float acc = 0.0f;
-    for (int r = r0; r < r1; ++r) acc += (float)X[(long long)r * ld + n];
-    parts[(long long)blockIdx.y * N + n] = acc;
+    if (n < N)
+        for (int s = grp; s < S; s += 4) acc += parts[(long long)s * N + n];
+    red[grp][c] = acc;
+    __syncthreads();
+    if (grp == 0 && n < N) out[n] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
 // out[i] = sum over s = 0 .. S-1 of parts[s * n + i], in that order.
@@ -64,12 +102,13 @@ __global__ __launch_bounds__(256) void sum_slabs_kernel(const float* __restrict_
 hipError_t colsum(const bf16* X, long long ld, int R, int N, float* parts, float* out,
                   hipStream_t stream) {
     const int chunks = (R + COLSUM_ROWS - 1) / COLSUM_ROWS;
-    hipLaunchKernelGGL(colsum_partial_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)chunks),
+    hipLaunchKernelGGL(colsum_partial_kernel,
+                       dim3((unsigned)((N + COLSUM_COLS - 1) / COLSUM_COLS), (unsigned)chunks),
                        dim3(256), 0, stream, X, ld, R, N, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
-                       parts, chunks, (long long)N, out);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream,
+                       parts, chunks, N, out);
     return hipGetLastError();
 }
 
