@@ -134,10 +134,11 @@ def _kernel_of(name: str):
     if "attn_bwd_dq_bf16_kernel" in name:  # <true>: the fused form attn_bwd launches
         return "attn_bwd_dq_preprocess" if ("<true>" in name or "ILb1E" in name) else "attn_bwd_dq"
     m = re.search(r"gemm_bf16_kernel<(\d), (\d), (\d+), (true|false)>", name)
-    if m:  # materialising path: operand orientations, output tile width, output type
+    if m:  # materialising path and attention block: orientations, tile width, output type
         ori = "".join("r" if x == "0" else "t" for x in m.group(1, 2))
-        return f"unfused_gemm_{ori}{m.group(3)}_{'f32' if m.group(4) == 'true' else 'bf16'}"
+        return f"gemm_{ori}{m.group(3)}_{'f32' if m.group(4) == 'true' else 'bf16'}"
     for k, tag in (("block_colsum", "colsum_partial_kernel"),
+                   ("block_colsum_final", "colsum_final_kernel"),
                    ("block_sum_slabs", "sum_slabs_kernel"),
                    ("unfused_softmax_bwd", "softmax_bwd_rows_kernel"),
                    ("unfused_softmax", "softmax_rows_kernel"),
