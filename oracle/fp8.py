@@ -50,6 +50,11 @@ error, puts 2^(z - m + 8) on the other side of a rounding midpoint.
 ``rounding_slack`` bounds what those two cases can change, given a bound on
 that rounding error.
 
+The backward (head_backward_fp8) keeps the same formats: every product runs
+on MXFP8 operands blocked along that product's own contraction (channels for
+Q K^T and dO V^T, positions for P^T dO, dS^T Q and dS K), the probabilities
+on the forward's fixed 2^-8 grid and dS on the block-scale rule of step 1.
+
 Pins: tests/test_oracle_fp8.py checks the encoding against the OFP8 table and
 brute-force nearest rounding, the scale rule against its defining inequality,
 the blocks against hand-built examples, and the attention against closed forms
@@ -74,6 +79,9 @@ __all__ = [
     "quantize_head",
     "head_forward_fp8",
     "forward_packed_fp8",
+    "quantize_positions",
+    "head_backward_fp8",
+    "backward_packed_fp8",
     "rounding_slack",
 ]
 
@@ -211,6 +219,98 @@ def head_forward_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray, return_parts: 
         parts.update({"z": z, "m": m, "p_hat": p_hat, "l": l})
         return o, lse, parts
     return o, lse
+
+
+def quantize_positions(x: np.ndarray):
+    """Blocks of 32 aligned positions per channel (zero past T): the blocking
+    of an operand whose product contracts over positions. x (T, d) ->
+    (codes (Tp, d), exps (Tp/32, d), dequantized (T, d)), Tp = round_up(T, 32)."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    Tp = -(-T // MX_BLOCK) * MX_BLOCK
+    pad = np.zeros((Tp, d))
+    pad[:T] = x
+    c, e, deq = quantize_blocks(pad, axis=0)
+    return c, e, deq[:T]
+
+
+def _quantize_rows_along(x: np.ndarray, axis: int):
+    """MX quantization of a T x T matrix in blocks of 32 along ``axis``,
+    padded with zeros to a multiple of 32 there; returns the dequantized
+    T x T values."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    Tp = -(-T // MX_BLOCK) * MX_BLOCK
+    pad = np.zeros((Tp, Tp))
+    pad[:T, :T] = x
+    return quantize_blocks(pad, axis=axis)[2][:T, :T]
+
+
+def head_backward_fp8(q, k, v, g, o, lse, return_parts: bool = False):
+    """FP8 backward of one head: gradients of L = sum(G * O) with every
+    product on MXFP8 operands, each blocked along its own contraction.
+
+    q, k, v, g (= dL/dO), o (the forward's O) are (T, d); lse (T,) is the
+    forward's natural-log LSE. Steps:
+      B1. Q, K, V, G blocked along channels (for the products over d) and
+          Q, K, G along positions (for the products over T).
+      B2. z = log2(e) Q^ K^T / sqrt(d) (channel blocks, causal);
+          P = 2^(z - lse log2 e), 0 above the diagonal.
+      B3. P^ = E4M3(2^8 P) 2^-8 (the forward's fixed grid; P <= 1.75).
+      B4. dV = P^T G^ (G blocked along positions).
+      B5. dP = G^ V^T (channel blocks); D = rowsum(G * O) on the unquantized
+          G and O; dS = P * (dP - D), with the unrounded P.
+      B6. dS quantized along queries (blocks of 32 queries of one key):
+          dK = dS_q^T Q^ / sqrt(d) (Q blocked along positions); along keys
+          (blocks of 32 keys of one query): dQ = dS_k K^ / sqrt(d).
+    Returns (dQ, dK, dV).
+    """
+    q, k, v, g, o = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, o))
+    lse = np.asarray(lse, dtype=np.float64)
+    T, d = q.shape
+    qc = quantize_blocks(q, axis=1)[2]
+    kc = quantize_blocks(k, axis=1)[2]
+    vc = quantize_blocks(v, axis=1)[2]
+    gc = quantize_blocks(g, axis=1)[2]
+    qp = quantize_positions(q)[2]
+    kp = quantize_positions(k)[2]
+    gp = quantize_positions(g)[2]
+    z = _logits(qc, kc)
+    p = np.exp2(z - LOG2E * lse[:, None])
+    if np.any(p > 1.75):
+        raise ValueError("lse below the row's scores: P exceeds the E4M3 grid of step B3")
+    p_hat = e4m3_decode(e4m3_encode(p * 2.0 ** P_SHIFT)) * 2.0 ** -P_SHIFT
+    dv = p_hat.T @ gp
+    dp = gc @ vc.T
+    dd = (g * o).sum(axis=1)
+    ds = p * (dp - dd[:, None])
+    scale = 1.0 / math.sqrt(d)
+    dk = scale * (_quantize_rows_along(ds, axis=0).T @ qp)
+    dq = scale * (_quantize_rows_along(ds, axis=1) @ kp)
+    if return_parts:
+        return dq, dk, dv, {"p": p, "p_hat": p_hat, "dp": dp, "d": dd, "ds": ds}
+    return dq, dk, dv
+
+
+def backward_packed_fp8(dout, qkv, out, lse, n_head: int, head_dim: int,
+                        heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """FP8 backward over packed arrays: dout, out (B, T, C), qkv (B, T, 3C),
+    lse (B, H, T) -> dqkv (B, T, 3C), float64; heads not listed stay NaN."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    B, T, C3 = qkv.shape
+    C = n_head * head_dim
+    dqkv = np.full((B, T, 3 * C), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(n_head)]
+    for b, h in pairs:
+        q, k, v = _split(qkv, b, h, n_head, head_dim)
+        lo = h * head_dim
+        g = np.asarray(dout, dtype=np.float64)[b, :, lo:lo + head_dim]
+        oo = np.asarray(out, dtype=np.float64)[b, :, lo:lo + head_dim]
+        dq, dk, dv = head_backward_fp8(q, k, v, g, oo, np.asarray(lse, dtype=np.float64)[b, h])
+        dqkv[b, :, lo:lo + head_dim] = dq
+        dqkv[b, :, C + lo:C + lo + head_dim] = dk
+        dqkv[b, :, 2 * C + lo:2 * C + lo + head_dim] = dv
+    return dqkv
 
 
 def _split(qkv: np.ndarray, b: int, h: int, n_head: int, head_dim: int):

@@ -319,6 +319,101 @@ def pin_rounding_slack(M):
     assert abs(ls_[1] - 2.0 ** -17 / (parts["l"][1] - 2.0 ** -17)) < 1e-18
 
 
+def _brute_backward(q, k, v, g, o, lse):
+    """FP8 backward steps B1-B6 in pure-Python loops from the brute-force
+    quantizers."""
+    T, d = q.shape
+    Tp = -(-T // 32) * 32
+
+    def chan(x):
+        out = np.zeros((T, d))
+        for t in range(T):
+            for c0 in range(0, d, 32):
+                out[t, c0:c0 + 32] = _quant_list(list(x[t, c0:c0 + 32]))[0]
+        return out
+
+    def pos(x):
+        pad = np.zeros((Tp, d))
+        pad[:T] = x
+        out = np.zeros((Tp, d))
+        for c in range(d):
+            for t0 in range(0, Tp, 32):
+                out[t0:t0 + 32, c] = _quant_list(list(pad[t0:t0 + 32, c]))[0]
+        return out[:T]
+
+    qc, kc, vc, gc = chan(q), chan(k), chan(v), chan(g)
+    qp, kp, gp = pos(q), pos(k), pos(g)
+    p = np.zeros((T, T))
+    ph = np.zeros((T, T))
+    ds = np.zeros((T, T))
+    for i in range(T):
+        dd = sum(g[i, c] * o[i, c] for c in range(d))
+        for j in range(i + 1):
+            z = sum(qc[i, c] * kc[j, c] for c in range(d)) / math.sqrt(d) * LOG2E
+            p[i, j] = 2.0 ** (z - lse[i] * LOG2E)
+            ph[i, j] = _nearest_value(p[i, j] * 256.0) / 256.0
+            dp = sum(gc[i, c] * vc[j, c] for c in range(d))
+            ds[i, j] = p[i, j] * (dp - dd)
+    dsq = np.zeros((Tp, Tp))   # blocks of 32 queries of one key
+    dsk = np.zeros((Tp, Tp))   # blocks of 32 keys of one query
+    pad = np.zeros((Tp, Tp))
+    pad[:T, :T] = ds
+    for a in range(Tp):
+        for b0 in range(0, Tp, 32):
+            dsq[b0:b0 + 32, a] = _quant_list(list(pad[b0:b0 + 32, a]))[0]
+            dsk[a, b0:b0 + 32] = _quant_list(list(pad[a, b0:b0 + 32]))[0]
+    dv = np.zeros((T, d))
+    dk = np.zeros((T, d))
+    dq = np.zeros((T, d))
+    for j in range(T):
+        for c in range(d):
+            dv[j, c] = sum(ph[i, j] * gp[i, c] for i in range(j, T))
+            dk[j, c] = sum(dsq[i, j] * qp[i, c] for i in range(j, T)) / math.sqrt(d)
+    for i in range(T):
+        for c in range(d):
+            dq[i, c] = sum(dsk[i, j] * kp[j, c] for j in range(i + 1)) / math.sqrt(d)
+    return dq, dk, dv
+
+
+def pin_backward_brute_force(M):
+    """The FP8 backward against pure-Python loops (forward outputs from the
+    brute force too)."""
+    cases = [RNG.standard_normal((4, T, 64)) * std for T, std in ((5, 1.0), (9, 2.0), (33, 0.7))]
+    # elements spread over 2^-10 .. 2^10 (Q and K less, to keep the scores
+    # moderate): block scales then differ between channel and position blocks
+    wide = RNG.standard_normal((4, 20, 64)) * np.exp2(RNG.integers(-10, 11, (4, 20, 64)))
+    wide[:2] *= 2.0 ** -8
+    cases.append(wide)
+    for q, k, v, g in cases:
+        o, lse = _brute_forward(q, k, v)
+        dq, dk, dv = M.head_backward_fp8(q, k, v, g, o, lse)
+        bq, bk, bv = _brute_backward(q, k, v, g, o, lse)
+        for a, b, name in ((dq, bq, "dq"), (dk, bk, "dk"), (dv, bv, "dv")):
+            assert np.allclose(a, b, rtol=1e-10, atol=1e-12), (name, np.abs(a - b).max())
+
+
+def pin_backward_zero_upstream(M):
+    """dO = 0: every gradient is exactly zero."""
+    T = 20
+    q, k, v = RNG.standard_normal((3, T, 64))
+    o, lse = M.head_forward_fp8(q, k, v)
+    for x in M.head_backward_fp8(q, k, v, np.zeros((T, 64)), o, lse):
+        assert np.all(x == 0)
+
+
+def pin_backward_near_exact(M):
+    """The FP8 backward stays within about 2^-3 (relative L2) of the exact
+    gradients on the unquantized inputs."""
+    T = 150
+    q, k, v, g = RNG.standard_normal((4, T, 64))
+    o, lse = M.head_forward_fp8(q, k, v)
+    got = M.head_backward_fp8(q, k, v, g, o, lse)
+    ref = A.head_backward(q, k, v, g)
+    for a, b in zip(got, ref):
+        rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+        assert 0 < rel < 0.12, rel
+
+
 PINS = [
     pin_e4m3_table,
     pin_e4m3_rounding,
@@ -332,6 +427,9 @@ PINS = [
     pin_near_exact_attention,
     pin_packed_layout,
     pin_rounding_slack,
+    pin_backward_brute_force,
+    pin_backward_zero_upstream,
+    pin_backward_near_exact,
 ]
 
 
@@ -436,7 +534,43 @@ def _forward_variant(kind):
     return f
 
 
+def _backward_variant(kind):
+    def f(q, k, v, g, o, lse, return_parts=False):
+        q, k, v, g, o = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, o))
+        T, d = q.shape
+        qc, kc, vc, gc = (F.quantize_blocks(a, axis=1)[2] for a in (q, k, v, g))
+        qp, kp, gp = (F.quantize_positions(a)[2] for a in (q, k, g))
+        if kind == "dk_q_channel_blocks":
+            qp = qc
+        if kind == "dv_g_channel_blocks":
+            gp = gc
+        z = F._logits(qc, kc)
+        p = np.exp2(z - LOG2E * np.asarray(lse)[:, None])
+        p_hat = F.e4m3_decode(F.e4m3_encode(p * 256.0)) / 256.0
+        dv = (p if kind == "dv_unquantized_p" else p_hat).T @ gp
+        dp = gc @ vc.T
+        dd = (g * o).sum(axis=1)
+        ds = (p_hat if kind == "ds_quantized_p" else p) * (dp - dd[:, None])
+        if kind == "ds_no_d":
+            ds = p * dp
+        sc = 1.0 / math.sqrt(d)
+        ax_k, ax_q = (1, 0) if kind == "ds_blocks_swapped" else (0, 1)
+        dk = sc * (F._quantize_rows_along(ds, axis=ax_k).T @ qp)
+        dq = sc * (F._quantize_rows_along(ds, axis=ax_q) @ kp)
+        if kind == "dq_no_scale":
+            dq = dq / sc
+        return dq, dk, dv
+    return f
+
+
 MUTANTS = {
+    "bwd_dv_unquantized_p": {"head_backward_fp8": _backward_variant("dv_unquantized_p")},
+    "bwd_ds_from_quantized_p": {"head_backward_fp8": _backward_variant("ds_quantized_p")},
+    "bwd_ds_without_d": {"head_backward_fp8": _backward_variant("ds_no_d")},
+    "bwd_ds_blocks_swapped": {"head_backward_fp8": _backward_variant("ds_blocks_swapped")},
+    "bwd_dk_q_channel_blocks": {"head_backward_fp8": _backward_variant("dk_q_channel_blocks")},
+    "bwd_dv_g_channel_blocks": {"head_backward_fp8": _backward_variant("dv_g_channel_blocks")},
+    "bwd_dq_no_scale": {"head_backward_fp8": _backward_variant("dq_no_scale")},
     "decode_bias_8": {"e4m3_decode": _decode_bias8},
     "encode_truncates": {"e4m3_encode": _encode_truncate},
     "encode_ties_away": {"e4m3_encode": _encode_ties_away},
