@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     AttnError,
     attn_block_bwd,
     attn_block_fwd,
+    attn_bwd_fp8,
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
@@ -21,15 +22,18 @@ from .binding import (  # noqa: F401
     attn_fwd_fp8,
     attn_fwd_unfused,
     attn_last_error,
+    attn_quantize_bwd_fp8,
     attn_quantize_fp8,
     attn_status_string,
     attn_version,
     backward,
+    backward_fp8,
     block_workspace_bytes,
     decode_workspace_floats,
     forward,
     forward_fp8,
     fp8_buffer_bytes,
+    fp8_bwd_buffer_bytes,
     lib,
     unfused_row_stride,
     unfused_workspace_bytes,

@@ -50,6 +50,9 @@ SIGNATURES = {
     "attn_block_fwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_block_bwd": ([_P] * 15 + [_I, _I, _I, _I, _P], _I),
     "attn_fp8_buffer_bytes": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_fp8_bwd_buffer_bytes": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_quantize_bwd_fp8": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_fp8": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_quantize_fp8": ([_P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_fp8": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
@@ -427,6 +430,55 @@ def forward(qkv, n_head: int, head_dim: int = 64, stream=None):
     lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
     attn_fwd(qkv, out, lse, n_head, head_dim, stream)
     return out, lse
+
+
+def fp8_bwd_buffer_bytes(B: int, T: int, n_head: int) -> int:
+    """Bytes of the FP8 backward buffer of attn_quantize_bwd_fp8 / attn_bwd_fp8."""
+    n = int(lib().attn_fp8_bwd_buffer_bytes(B, T, n_head))
+    if n < 0:
+        raise ValueError("B, T and n_head must be non-negative")
+    return n
+
+
+def attn_quantize_bwd_fp8(dout, qkv, out, lse, fp8_bwd, n_head: int, head_dim: int = 64,
+                          stream=None) -> None:
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    _require(dout, "dout", torch.bfloat16, (B, T, C))
+    _require(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _require(out, "out", torch.bfloat16, (B, T, C))
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _require_bytes(fp8_bwd, "fp8_bwd", fp8_bwd_buffer_bytes(B, T, n_head))
+    _check(lib().attn_quantize_bwd_fp8(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(fp8_bwd),
+                                       B, T, n_head, head_dim, _stream_ptr(stream)),
+           "attn_quantize_bwd_fp8")
+
+
+def attn_bwd_fp8(fp8, fp8_bwd, dqkv, n_head: int, head_dim: int = 64, stream=None) -> None:
+    """fp8 / fp8_bwd: the buffers of attn_quantize_fp8 and attn_quantize_bwd_fp8
+    for these shapes; dqkv (B, T, 3C) bf16 gives B and T."""
+    torch = _torch()
+    B, T, C = _dims(dqkv, n_head, head_dim)
+    _require(dqkv, "dqkv", torch.bfloat16, (B, T, 3 * C))
+    _require_bytes(fp8, "fp8", fp8_buffer_bytes(B, T, n_head))
+    _require_bytes(fp8_bwd, "fp8_bwd", fp8_bwd_buffer_bytes(B, T, n_head))
+    _check(lib().attn_bwd_fp8(_ptr(fp8), _ptr(fp8_bwd), _ptr(dqkv), B, T, n_head, head_dim,
+                              _stream_ptr(stream)), "attn_bwd_fp8")
+
+
+def backward_fp8(dout, qkv, out, lse, n_head: int, head_dim: int = 64, stream=None):
+    """dqkv of the FP8 backward for the FP8 forward that produced (out, lse)
+    on qkv: quantize the forward and backward operands into new buffers, then
+    attn_bwd_fp8."""
+    torch = _torch()
+    B, T, C = _dims(qkv, n_head, head_dim)
+    f8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+    b8 = torch.empty(fp8_bwd_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+    dqkv = torch.empty_like(qkv)
+    attn_quantize_fp8(qkv, f8, n_head, head_dim, stream)
+    attn_quantize_bwd_fp8(dout, qkv, out, lse, b8, n_head, head_dim, stream)
+    attn_bwd_fp8(f8, b8, dqkv, n_head, head_dim, stream)
+    return dqkv
 
 
 def forward_fp8(qkv, n_head: int, head_dim: int = 64, stream=None):

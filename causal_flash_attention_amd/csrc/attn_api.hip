@@ -27,6 +27,10 @@ hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, co
                                        void*, int, int, int, hipStream_t);
 long long fp8_buffer_bytes(int B, int T, int H);
 long long block_workspace_floats(int B, int T, int H);
+long long fp8_bwd_buffer_bytes(int B, int T, int H);
+hipError_t launch_attn_quantize_bwd_fp8(const void*, const void*, const void*, const float*, void*,
+                                        int, int, int, hipStream_t);
+hipError_t launch_attn_bwd_fp8(const void*, const void*, void*, int, int, int, hipStream_t);
 hipError_t launch_attn_block_fwd_bf16(const void*, const void*, const void*, const void*,
                                       const void*, void*, void*, float*, void*, int, int, int,
                                       hipStream_t);
@@ -506,6 +510,58 @@ int attn_block_bwd(const void* dy, const void* x, const void* w_attn, const void
         dy, x, w_attn, w_proj, qkv, att, lse, datt, dqkv, dx, dw_attn, db_attn, dw_proj, db_proj,
         ws, B, T, H, as_stream(stream));
     return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_block_bwd launch");
+}
+
+long long attn_fp8_bwd_buffer_bytes(int B, int T, int n_head) {
+    if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    return cattn::fp8_bwd_buffer_bytes(B, T, n_head);
+}
+
+int attn_quantize_bwd_fp8(const void* dout, const void* qkv, const void* out, const float* lse,
+                          void* fp8_bwd, int B, int T, int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!dout || !qkv || !out || !lse || !fp8_bwd))
+        return fail(ATTN_ERR_NULL_PTR, "dout, qkv, out, lse and fp8_bwd must not be NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_fp8(T)) != ATTN_OK) return st;
+    const void* al16[] = {dout, qkv, out, fp8_bwd};
+    if ((st = check_all_aligned(al16, 4, 16, "dout, qkv, out and fp8_bwd must be 16-byte aligned")) != ATTN_OK)
+        return st;
+    if ((st = check_aligned(lse, 4, "lse must be 4-byte aligned")) != ATTN_OK) return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const Span ins[] = {span(dout, z.bt_c, "dout"), span(qkv, z.qkv, "qkv"), span(out, z.bt_c, "out"),
+                        span(lse, z.rows, "lse")};
+    const Span outs[] = {span(fp8_bwd, cattn::fp8_bwd_buffer_bytes(B, T, H), "fp8_bwd")};
+    if ((st = check_disjoint(outs, 1, ins, 4)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_quantize_bwd_fp8(dout, qkv, out, lse, fp8_bwd, B, T, H,
+                                                             as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_quantize_bwd_fp8 launch");
+}
+
+int attn_bwd_fp8(const void* fp8, const void* fp8_bwd, void* dqkv, int B, int T, int n_head,
+                 int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    const int H = n_head;
+    if (!(B == 0 || T == 0 || H == 0) && (!fp8 || !fp8_bwd || !dqkv))
+        return fail(ATTN_ERR_NULL_PTR, "fp8, fp8_bwd and dqkv must not be NULL");
+    bool empty = false;
+    int st = check_shape(B, T, H, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_fp8(T)) != ATTN_OK) return st;
+    const void* al16[] = {fp8, fp8_bwd, dqkv};
+    if ((st = check_all_aligned(al16, 3, 16, "fp8, fp8_bwd and dqkv must be 16-byte aligned")) != ATTN_OK)
+        return st;
+    const Sizes z = sizes(B, T, H, 2);
+    const Span ins[] = {span(fp8, cattn::fp8_buffer_bytes(B, T, H), "fp8"),
+                        span(fp8_bwd, cattn::fp8_bwd_buffer_bytes(B, T, H), "fp8_bwd")};
+    const Span outs[] = {span(dqkv, z.qkv, "dqkv")};
+    if ((st = check_disjoint(outs, 1, ins, 2)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_attn_bwd_fp8(fp8, fp8_bwd, dqkv, B, T, H, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_bwd_fp8 launch");
 }
 
 long long attn_fp8_buffer_bytes(int B, int T, int n_head) {

@@ -269,6 +269,34 @@ int attn_quantize_fp8(const void* qkv, void* fp8, int B, int T, int n_head, int 
 int attn_fwd_fp8(const void* fp8, void* out, float* lse, int B, int T, int n_head, int head_dim,
                  void* stream);
 
+/* FP8 backward: the gradients of L = sum(dout * out) for the FP8 forward,
+ * with every product on MXFP8 operands blocked along its own contraction
+ * (channels for S = Q K^T and dP = dout V^T; positions for dV = P^T dout,
+ * dK = dS^T Q / sqrt(d) and dQ = dS K / sqrt(d)). P = exp(S - lse) enters dV
+ * on the forward's fixed grid E4M3(2^8 P) 2^-8; D = rowsum(dout * out);
+ * dS = P (dP - D) is quantized per block of 32 queries (for dK) or 32 keys
+ * (for dQ) with the forward's block-scale rule.
+ * attn_quantize_bwd_fp8 reads dout and out (B, T, C) bf16, qkv, and lse
+ * (B, n_head, T) float32 from attn_fwd_fp8, and writes the backward buffer
+ * fp8_bwd (caller-owned, attn_fp8_bwd_buffer_bytes(B, T, n_head) bytes,
+ * 16-byte aligned). With BH, Tp, NT as above and n = 64 BH Tp:
+ *   [0, n) V codes in channel blocks [BH][Tp][64]; [n, 2n) dout likewise;
+ *   [2n, 3n) Q codes in position blocks [BH][64][Tp]; [3n, 4n) K likewise;
+ *   [4n, 5n) dout likewise; then BH * NT tiles of 1152 bytes per 64
+ *   positions: exponent bytes of V (channel blocks, 2 per position), K
+ *   (position blocks, 64 per block of 32 positions), dout (channel blocks),
+ *   Q and dout (position blocks), 128 bytes each; then the tile's
+ *   LSE * log2(e) (+inf past T) and D (0 past T), 64 floats each.
+ * attn_bwd_fp8 reads the forward buffer fp8 (attn_quantize_fp8 on the same
+ * qkv) and fp8_bwd, and overwrites dqkv (B, T, 3C) bf16: two kernels on
+ * `stream`, no atomics (deterministic), nothing allocated; the limits of the
+ * forward apply. */
+long long attn_fp8_bwd_buffer_bytes(int B, int T, int n_head);
+int attn_quantize_bwd_fp8(const void* dout, const void* qkv, const void* out, const float* lse,
+                          void* fp8_bwd, int B, int T, int n_head, int head_dim, void* stream);
+int attn_bwd_fp8(const void* fp8, const void* fp8_bwd, void* dqkv, int B, int T, int n_head,
+                 int head_dim, void* stream);
+
 /* ------------------------------------------------------------- status ---- */
 
 /* Static, human-readable name of a status code (never NULL). */

@@ -48,6 +48,7 @@ def test_header_declares_expected_entry_points():
               "attn_decode", "attn_decode_workspace_floats",
               "attn_fp8_buffer_bytes", "attn_quantize_fp8", "attn_fwd_fp8",
               "attn_block_fwd", "attn_block_bwd", "attn_block_workspace_bytes",
+              "attn_fp8_bwd_buffer_bytes", "attn_quantize_bwd_fp8", "attn_bwd_fp8",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -249,6 +250,32 @@ def test_block_workspace_size(L):
     assert L.attn_block_workspace_bytes(1, 1, 1) >= 4 * (10 * 64 + 64 * 192)
     assert L.attn_block_workspace_bytes(0, 5, 2) == 0
     assert L.attn_block_workspace_bytes(1, -1, 2) == -1
+
+
+@no_gpu_only
+def test_fp8_bwd_validation(L):
+    F8, B8 = 0x70000000, 0x78000000
+    fq, fb = L.attn_quantize_bwd_fp8, L.attn_bwd_fp8
+    ok = (1, 64, 2, 64)
+    assert fq(G, Q, O, LS, None, *ok, None) == -1
+    assert fq(G, Q, O, LS, B8 + 8, *ok, None) == -5
+    assert fq(G, Q, O, LS + 1, B8, *ok, None) == -5
+    assert fq(G, Q, O, LS, Q + 64, *ok, None) == -6            # buffer inside qkv
+    assert fq(G, Q, O, LS, B8, 1, 64, 2, 32, None) == -3
+    assert fb(F8, B8, None, *ok, None) == -1
+    assert fb(F8, B8, DQ + 8, *ok, None) == -5
+    assert fb(F8, B8, B8 + 256, *ok, None) == -6               # dqkv inside the buffer
+    assert fb(F8, B8, DQ, 1, 67108801, 1, 64, None) == -4
+    assert fq(None, None, None, None, None, 0, 64, 2, 64, None) == 0
+    assert fb(None, None, None, 1, 0, 2, 64, None) == 0
+
+
+def test_fp8_bwd_buffer_size(L):
+    # 320 code bytes per (head, padded position) plus 1152 side bytes per tile
+    assert L.attn_fp8_bwd_buffer_bytes(1, 64, 1) == 320 * 64 + 1152
+    assert L.attn_fp8_bwd_buffer_bytes(2, 65, 3) == 6 * (320 * 128 + 2 * 1152)
+    assert L.attn_fp8_bwd_buffer_bytes(0, 5, 2) == 0
+    assert L.attn_fp8_bwd_buffer_bytes(1, -1, 2) == -1
 
 
 def test_fp8_buffer_size(L):
