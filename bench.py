@@ -61,7 +61,10 @@ STAGES = list(KERNELS)
 # Kernels outside the step whose HBM traffic is also recorded: the decode pass.
 EXTRA_TRAFFIC = {"decode_partial": ("attn_decode_bf16.hip",),
                  "attn_quantize_fp8": ("attn_fp8.hip",),
-                 "attn_fwd_fp8": ("attn_fp8.hip",)}
+                 "attn_fwd_fp8": ("attn_fp8.hip",),
+                 "attn_quantize_bwd_fp8": ("attn_fp8_bwd.hip",),
+                 "attn_bwd_fp8_dkdv": ("attn_fp8_bwd.hip",),
+                 "attn_bwd_fp8_dq": ("attn_fp8_bwd.hip",)}
 
 
 def parse_args(argv=None):
@@ -145,6 +148,9 @@ def _kernel_of(name: str):
                    ("decode_partial", "decode_partial_kernel"),
                    ("decode_combine", "decode_combine_kernel"),
                    ("attn_fwd_fp8", "attn_fwd_fp8_kernel"),
+                   ("attn_bwd_fp8_dq", "attn_bwd_fp8_dq_kernel"),
+                   ("attn_bwd_fp8_dkdv", "attn_bwd_fp8_dkdv_kernel"),
+                   ("attn_quantize_bwd_fp8", "attn_quantize_bwd_fp8_kernel"),
                    ("attn_quantize_fp8", "attn_quantize_fp8_kernel")):
         if tag in name:
             return k
@@ -405,7 +411,8 @@ def time_block(w, attn_step_us, stream, calls=50):
                                         "step minus the attention step"}}
 
 
-def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, calls=100):
+def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, dout=None, dqkv_bf16=None, step_bf16_us=None,
+             calls=100):
     """The FP8 forward on the step's qkv: quantize and forward timed apart and
     together; the forward's FLOP rate against the FP8 MFMA peak, the
     quantization's HBM rate (bf16 qkv read, FP8 buffer written)."""
@@ -443,13 +450,38 @@ def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, calls=100):
         return 1000.0 * e0.elapsed_time(e1) / calls
 
     q_us, f_us, p_us = timed(quant), timed(fwd), timed(both)
+    bwd_part = None
+    if dout is not None:
+        b8 = torch.empty(binding.fp8_bwd_buffer_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+        dqkv = torch.empty_like(qkv)
+
+        def qbwd():
+            binding.attn_quantize_bwd_fp8(dout, qkv, out, lse, b8, H, D, stream)
+
+        def bwd():
+            binding.attn_bwd_fp8(buf, b8, dqkv, H, D, stream)
+
+        def step():
+            quant()
+            fwd()
+            qbwd()
+            bwd()
+
+        qb_us, b_us, s_us = timed(qbwd), timed(bwd), timed(step)
+        ref = dqkv_bf16.float()
+        rel_g = float(torch.linalg.vector_norm(dqkv.float() - ref) / torch.linalg.vector_norm(ref))
+        counted = w.counted_flops()
+        bwd_part = {"quantize_bwd_us": qb_us, "bwd_us": b_us, "bwd_tflops": counted["bwd"] / (b_us * 1e-6) / 1e12,
+                    "step_us": s_us, "step_tflops": counted["total"] / (s_us * 1e-6) / 1e12,
+                    "step_speedup_vs_bf16": (step_bf16_us / s_us) if step_bf16_us else None,
+                    "rel_l2_dqkv_vs_bf16": rel_g}
     fwd_flops = 2.0 * B * H * T * T * D  # S = QK^T and O = PV, causal halves counted
     tf = fwd_flops / (f_us * 1e-6) / 1e12
     qbytes = 3.0 * B * T * C * 2 + nbuf
     gbs = qbytes / (q_us * 1e-6) / 1e9
     ref = out_bf16.float()
     rel = float(torch.linalg.vector_norm(out.float() - ref) / torch.linalg.vector_norm(ref))
-    return {"workload": w.name, "quantize_us": q_us, "fwd_us": f_us, "pass_us": p_us,
+    res = {"workload": w.name, "quantize_us": q_us, "fwd_us": f_us, "pass_us": p_us,
             "calls": calls, "fwd_tflops": tf, "pass_tflops": fwd_flops / (p_us * 1e-6) / 1e12,
             "fwd_speedup_vs_bf16_fwd": fwd_bf16_us / f_us,
             "rel_l2_vs_bf16_fwd": rel,
@@ -461,6 +493,9 @@ def time_fp8(w, qkv, out_bf16, fwd_bf16_us, stream, calls=100):
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                   "bytes_per_call": qbytes,
                                   "traffic": traffic_from_profile("attn_quantize_fp8", w.name)}}
+    if bwd_part is not None:
+        res["backward"] = bwd_part
+    return res
 
 
 def main(argv=None):
@@ -564,7 +599,11 @@ def main(argv=None):
         attn_fwd_out = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
         attn_fwd_lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         binding.attn_fwd(qkv, attn_fwd_out, attn_fwd_lse, H, D, stream)
-        fp8 = time_fp8(w, qkv, attn_fwd_out, kernel_us["attn_fwd"], stream)
+        attn_dqkv = torch.empty_like(qkv)
+        attn_delta = torch.empty_like(delta)
+        binding.attn_bwd(dout, qkv, attn_fwd_out, attn_fwd_lse, attn_dqkv, attn_delta, H, D, stream)
+        fp8 = time_fp8(w, qkv, attn_fwd_out, kernel_us["attn_fwd"], stream, dout=dout,
+                       dqkv_bf16=attn_dqkv, step_bf16_us=ms_per_step * 1000.0)
     else:
         fp8 = None
 
