@@ -71,17 +71,22 @@ __device__ __forceinline__ i32x4 tile_rsrc(const bf16* p, long long ld, int rows
     return buffer_rsrc(p, (unsigned int)n);
 }
 
-// MFMA operand of 32 rows (outer) x 16 k from a row-oriented tile: lane l%32
-// takes row `r`, k = 16kc + {4hf..4hf+3, 8+4hf..8+4hf+3} (two 8-byte reads),
-// the k order the transposing reads produce.
+// The products here relabel k inside each 16-chunk so that lane half h
+// holds k = 16kc + 8h .. 8h + 7 of both operands (any labelling works when
+// both operands use it): a row-oriented operand is then one 16-byte LDS read
+// per lane, and the transposing reads take tile rows 8h + i/4 and 8h + 4 +
+// i/4 (lane i of each 16-lane group) instead of the attention kernels' 4h and
+// 8 + 4h. Both read patterns stay free of bank conflicts under swz.
 __device__ __forceinline__ bf16x8 row_operand(lds_bf16* tile, int r, int kc, int hf) {
-    typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
-    const int s = swz(r);
-    const lds_bf16* row = tile + r * 64 + 4 * hf;
-    const u32x2 a = *reinterpret_cast<lds_u32x2*>(row + (((2 * kc) ^ s) << 3));
-    const u32x2 b = *reinterpret_cast<lds_u32x2*>(row + (((2 * kc + 1) ^ s) << 3));
-    const u32x4 v = {a[0], a[1], b[0], b[1]};
-    return as_bf16x8(v);
+    return atile_row(tile, r, 2 * kc + hf);
+}
+
+__device__ __forceinline__ void gemm_tr_offsets(int lane, int db, int* off0, int* off1) {
+    const int i = lane & 15, grp = lane >> 4, h = grp >> 1;
+    const int d = db * 32 + 16 * (grp & 1) + 4 * (i & 3);
+    const int r0 = 8 * h + (i >> 2), r1 = r0 + 4;
+    *off0 = r0 * 64 + (((d >> 3) ^ swz(r0)) << 3) + (d & 7);
+    *off1 = r1 * 64 + (((d >> 3) ^ swz(r1)) << 3) + (d & 7);
 }
 
 // C[M x N] = alpha * A[M x K] B[K x N] per head; BN = 128 (waves 2 x 2, each
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
     const int wn0 = BN == 128 ? (wave >> 1) * 64 : 0;
     int troff[2][2];
 #pragma unroll
-    for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &troff[db][0], &troff[db][1]);
+    for (int db = 0; db < 2; ++db) gemm_tr_offsets(lane, db, &troff[db][0], &troff[db][1]);
 
     // Tile t (0 .. NB-1) of an operand for k step k0: a row operand's tile t
     // holds rows outer0 + 64t .. +63 and k0 .. k0 + 63; a tr operand's tile t
