@@ -23,7 +23,13 @@ against the 8 TB/s roofline; ``block`` times the whole attention layer
 (attn_block_fwd + attn_block_bwd: c_attn, attention, c_proj and their
 gradients) at the same shape; ``fp8`` times the FP8 forward (attn_quantize_fp8
 then attn_fwd_fp8) on the same qkv, against the FP8 MFMA peak, and reports
-how far its output lies from the bf16 forward's.
+how far its output lies from the bf16 forward's. ``split_us`` gives the
+median forward, backward and step times of the kernel-timing pass; ``cold``
+times single steps after a 512 MiB scratch write (inputs out of every
+cache); ``hbm`` is the step's algorithmic HBM rate; ``b64`` times the same
+step at batch 64; ``peaks`` measures the chip's sustained bf16 MFMA rate (and
+the clock it ran at) and its HBM copy rate with the library's probes, next to
+the specification peaks the roofline uses.
 """
 
 from __future__ import annotations
@@ -33,6 +39,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -81,6 +88,9 @@ def parse_args(argv=None):
     p.add_argument("--no-decode", action="store_true", help="skip timing decode")
     p.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 forward")
     p.add_argument("--no-block", action="store_true", help="skip timing the attention layer")
+    p.add_argument("--no-b64", action="store_true", help="skip the step at batch 64")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the MFMA and HBM peak probes")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -151,7 +161,10 @@ def _kernel_of(name: str):
                    ("attn_bwd_fp8_dq", "attn_bwd_fp8_dq_kernel"),
                    ("attn_bwd_fp8_dkdv", "attn_bwd_fp8_dkdv_kernel"),
                    ("attn_quantize_bwd_fp8", "attn_quantize_bwd_fp8_kernel"),
-                   ("attn_quantize_fp8", "attn_quantize_fp8_kernel")):
+                   ("attn_quantize_fp8", "attn_quantize_fp8_kernel"),
+                   ("peak_mfma", "peak_mfma_kernel"),
+                   ("peak_copy", "peak_copy_kernel"),
+                   ("peak_read", "peak_read_kernel")):
         if tag in name:
             return k
     for k, tag in (("attn_fwd", "attn_fwd_bf16_kernel"), ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
@@ -254,15 +267,149 @@ def cpu_baseline(w, target_s: float):
         if el >= target_s or done >= w.B * w.n_head:
             break
     flops = 7.0 * done * w.T * w.T * D
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     return {
         "value": flops / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {w.B * w.n_head} heads of {w.name} (T={w.T}, d={D}), float64 "
-                  f"forward+backward materialising T x T per head, {el:.1f} s wall, "
+        "sample": f"{done} head passes of {w.name} (T={w.T}, d={D}; the {w.n_head} heads of batch "
+                  f"row 0 in turn, {w.B * w.n_head} passes being the whole workload's count), "
+                  f"float64 forward+backward materialising T x T per head, {el:.1f} s wall, "
                   f"counted 7*T^2*d FLOPs per head",
+        "wall_s": el,
+        "cpu_model": model,
+        "cpu_count": os.cpu_count(),
+        "affinity_cpus": affinity,
     }
+
+
+def step_hbm_bytes(w) -> float:
+    """Bytes the three kernels of a step must move at least once, with
+    X = B*H*T*d elements and R = B*H*T rows: forward qkv + out + lse
+    (8X + 4R); dQ with the preprocess q, k, v, dout, out, lse in and dQ plus
+    the 40-byte workspace rows out (12X + 44R); dK/dV q, k, v, dout and the
+    32-byte workspace terms in, dK and dV out (12X + 32R)."""
+    X = float(w.B) * w.n_head * w.T * w.head_dim
+    R = float(w.B) * w.n_head * w.T
+    return 32.0 * X + 80.0 * R
+
+
+def time_cold(step, stream, dev, n):
+    """Steps timed one by one after a 512 MiB scratch write, which evicts the
+    inputs from the caches (the 256 MB Infinity Cache included)."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(1000.0 * e0.elapsed_time(e1))
+    del scratch
+    return {"us_per_step": statistics.median(times), "steps": n, "scratch_mib": 512,
+            "what": "median of single steps, each after a 512 MiB scratch write"}
+
+
+def time_other_batch(w, stream, dev, K):
+    """The same step at another batch size (GPT-2 124M layer shape at B = 64)."""
+    import numpy as np
+    import torch
+    from causal_flash_attention_amd import binding
+    from causal_flash_attention_amd import inputs as I
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    qh, gh = I.attention_inputs(B, T, H, D, w.dtype, w.qkv_std, w.dout_std, seed=0)
+    qkv = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
+    dout = torch.from_numpy(gh.view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dqkv = torch.empty_like(qkv)
+    delta = torch.empty(binding.workspace_floats(B, T, H), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.attn_fwd(qkv, out, lse, H, D, stream)
+        binding.attn_bwd(dout, qkv, out, lse, dqkv, delta, H, D, stream)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / K
+    tflops = w.counted_flops()["total"] / (us * 1e-6) / 1e12
+    return {"workload": w.name, "us_per_step": us, "steps": K, "tflops": tflops,
+            "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
+
+
+def measure_peaks(stream, dev):
+    """The chip's sustained bf16 MFMA rate (attn_peak_mfma: register-only
+    MFMA chains on every SIMD) with the clock it ran at, and its HBM copy
+    rate (attn_peak_copy over 1 GiB, read + write bytes counted) and read rate
+    (attn_peak_read over the same 1 GiB)."""
+    import torch
+    from causal_flash_attention_amd import binding
+    n_wg, iters = 2048, 4096
+    flops = binding.attn_peak_mfma_flops(n_wg, iters)
+    out = torch.empty(256 * n_wg, dtype=torch.float32, device=dev)
+    ticks = torch.empty(2 * n_wg, dtype=torch.int64, device=dev)
+    binding.attn_peak_mfma(out, ticks, n_wg, iters, stream)
+    rates = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        binding.attn_peak_mfma(out, ticks, n_wg, iters, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    t = ticks.view(n_wg, 2).cpu().double()
+    clock_ghz = float((t[:, 0] / t[:, 1]).median()) * 0.1  # constant clock: 100 MHz
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        binding.attn_peak_copy(src, dst, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        binding.attn_peak_copy(src, dst, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del dst
+    slots = torch.zeros(binding.lib().attn_peak_read_slots(), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.attn_peak_read(src, slots, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        binding.attn_peak_read(src, slots, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = float(nbytes) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, slots
+    return {"mfma_bf16_tflops": max(rates), "mfma_clock_ghz": clock_ghz,
+            "mfma_spec_tflops": BF16_PEAK_TFLOPS, "hbm_copy_gbs": copy_gbs,
+            "hbm_read_gbs": read_gbs, "hbm_spec_gbs": HBM_PEAK_GBS,
+            "what": "attn_peak_mfma (register-only bf16 32x32x16 MFMA chains, every SIMD), "
+                    "attn_peak_copy (1 GiB device copy, read + write bytes) and attn_peak_read "
+                    "(1 GiB read)"}
 
 
 def time_unfused(w, qkv, dout, stream, K):
@@ -577,6 +724,10 @@ def main(argv=None):
     kernel_us = {}
     for j, name in enumerate(STAGES):
         kernel_us[name] = 1000.0 * sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+    split_us = {"fwd": statistics.median(1000.0 * e[0].elapsed_time(e[1]) for e in ev),
+                "bwd": statistics.median(1000.0 * e[1].elapsed_time(e[-1]) for e in ev),
+                "step": statistics.median(1000.0 * e[0].elapsed_time(e[-1]) for e in ev)}
+    cold = time_cold(step, stream, dev, min(K, 20))
 
     flops = w.counted_flops()
     tflops = flops["total"] / (ms_per_step * 1e-3) / 1e12
@@ -591,6 +742,16 @@ def main(argv=None):
     roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
             "kernel": dom}
+
+    step_bytes = step_hbm_bytes(w)
+    hbm = {"algorithmic_bytes": step_bytes, "gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+           "peak": HBM_PEAK_GBS,
+           "what": "bytes each kernel of the step must read and write once (qkv, out, lse, dout, "
+                   "dqkv and the backward workspace), over the step time"}
+    hbm["frac"] = hbm["gbs"] / HBM_PEAK_GBS
+    b64 = None if args.no_b64 else time_other_batch(BY_NAME["gpt2_124m_b64_t1024"], stream, dev,
+                                                     min(K, 50))
+    peaks = None if args.no_peaks else measure_peaks(stream, dev)
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
     decode = None if args.no_decode else time_decode(stream)
@@ -632,9 +793,17 @@ def main(argv=None):
                    "counted_gflop_per_step": flops["total"] / 1e9},
         "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "kernels_us": kernel_us,
+        "split_us": split_us,
+        "cold": cold,
+        "hbm": hbm,
         "host_wall_s": wall,
         "roofline": roof,
     }
+    if peaks is not None:
+        result["peaks"] = peaks
+        result["pct_of_measured_bf16_peak"] = 100.0 * tflops / peaks["mfma_bf16_tflops"]
+    if b64 is not None:
+        result["b64"] = b64
     if unfused is not None:
         unfused["fa_speedup"] = unfused["ms_per_step"] / ms_per_step
         result["unfused"] = unfused

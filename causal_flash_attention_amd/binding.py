@@ -57,6 +57,11 @@ SIGNATURES = {
     "attn_fwd_fp8": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_fwd_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_f32": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_peak_mfma_flops": ([_I, _I], ctypes.c_longlong),
+    "attn_peak_mfma": ([_P, _P, _I, _I, _P], _I),
+    "attn_peak_copy": ([_P, _P, ctypes.c_longlong, _P], _I),
+    "attn_peak_read_slots": ([], _I),
+    "attn_peak_read": ([_P, ctypes.c_longlong, _P, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_version": ([], _I),
@@ -404,6 +409,48 @@ def attn_fwd_fp8(fp8, out, lse, n_head: int, head_dim: int = 64, stream=None) ->
     _require_bytes(fp8, "fp8", fp8_buffer_bytes(B, T, n_head))
     _check(lib().attn_fwd_fp8(_ptr(fp8), _ptr(out), _ptr(lse), B, T, n_head, head_dim,
                               _stream_ptr(stream)), "attn_fwd_fp8")
+
+
+def attn_peak_mfma_flops(n_wg: int, iters: int) -> int:
+    """bf16 MFMA FLOPs of one attn_peak_mfma call with these arguments."""
+    n = int(lib().attn_peak_mfma_flops(n_wg, iters))
+    if n < 0:
+        raise ValueError("n_wg and iters must lie in [1, 2^20]")
+    return n
+
+
+def attn_peak_mfma(out, ticks, n_wg: int, iters: int, stream=None) -> None:
+    """MFMA peak probe: out (n_wg * 256,) float32 and ticks (2 * n_wg,) int64
+    GPU tensors (see causal_attn.h)."""
+    torch = _torch()
+    _require(out, "out", torch.float32, (256 * n_wg,))
+    _require(ticks, "ticks", torch.int64, (2 * n_wg,))
+    _check(lib().attn_peak_mfma(_ptr(out), _ptr(ticks), n_wg, iters, _stream_ptr(stream)),
+           "attn_peak_mfma")
+
+
+def attn_peak_copy(src, dst, stream=None) -> None:
+    """HBM probe: copies the contiguous GPU tensor src into dst (same size in
+    bytes, a multiple of 16)."""
+    if src is None or dst is None:
+        raise ValueError("src and dst are required")
+    if not src.is_cuda or not dst.is_cuda:
+        raise ValueError("src and dst must be GPU tensors")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous and of the same size in bytes")
+    _check(lib().attn_peak_copy(_ptr(src), _ptr(dst), n, _stream_ptr(stream)), "attn_peak_copy")
+
+
+def attn_peak_read(src, out, stream=None) -> None:
+    """HBM read probe: reads the contiguous GPU tensor src; out is an int32
+    GPU tensor of attn_peak_read_slots() elements."""
+    torch = _torch()
+    if src is None or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _require(out, "out", torch.int32, (int(lib().attn_peak_read_slots()),))
+    n = src.numel() * src.element_size()
+    _check(lib().attn_peak_read(_ptr(src), n, _ptr(out), _stream_ptr(stream)), "attn_peak_read")
 
 
 def attn_status_string(status: int) -> str:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip",
            "attn_unfused_bf16.hip", "attn_decode_bf16.hip", "attn_fp8.hip",
-           "attn_fp8_bwd.hip", "attn_block_bf16.hip"]
+           "attn_fp8_bwd.hip", "attn_block_bf16.hip", "peak_probe.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 add/mul/fma,
 # which are avoided on this target; hipcc's host pass warns that it does not

@@ -47,6 +47,11 @@ hipError_t launch_attn_bwd_dkdv_f32(const float*, const float*, const float*, co
                                     int, int, int, hipStream_t);
 hipError_t launch_attn_bwd_dq_f32(const float*, const float*, const float*, const float*, float*,
                                   int, int, int, hipStream_t);
+long long peak_mfma_flops_per_wg(int iters);
+hipError_t launch_peak_mfma(float*, long long*, int, int, hipStream_t);
+hipError_t launch_peak_copy(const void*, void*, long long, hipStream_t);
+int peak_read_slots();
+hipError_t launch_peak_read(const void*, long long, unsigned int*, hipStream_t);
 }  // namespace cattn
 
 namespace {
@@ -643,5 +648,63 @@ const char* attn_status_string(int status) {
 const char* attn_last_error(void) { return g_last_error; }
 
 int attn_version(void) { return kVersion; }
+
+constexpr int kPeakMax = 1 << 20;
+
+long long attn_peak_mfma_flops(int n_wg, int iters) {
+    if (n_wg < 1 || n_wg > kPeakMax || iters < 1 || iters > kPeakMax) return -1;
+    return (long long)n_wg * cattn::peak_mfma_flops_per_wg(iters);
+}
+
+int attn_peak_mfma(float* out, long long* ticks, int n_wg, int iters, void* stream) {
+    g_last_error[0] = '\0';
+    if (!out || !ticks) return fail(ATTN_ERR_NULL_PTR, "attn_peak_mfma: out or ticks is NULL");
+    if (n_wg < 1 || n_wg > kPeakMax || iters < 1 || iters > kPeakMax)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_peak_mfma: n_wg and iters must lie in [1, 2^20]");
+    int st;
+    if ((st = check_aligned(out, 4, "out must be 4-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(ticks, 8, "ticks must be 8-byte aligned")) != ATTN_OK) return st;
+    const Span outs[1] = {{(uintptr_t)out, (uintptr_t)(out + 256LL * n_wg), "out"}};
+    const Span ins[1] = {{(uintptr_t)ticks, (uintptr_t)(ticks + 2LL * n_wg), "ticks"}};
+    if ((st = check_disjoint(outs, 1, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_peak_mfma(out, ticks, n_wg, iters, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_peak_mfma launch");
+}
+
+int attn_peak_copy(const void* src, void* dst, long long bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (bytes == 0) return ATTN_OK;
+    if (!src || !dst) return fail(ATTN_ERR_NULL_PTR, "attn_peak_copy: src or dst is NULL");
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_peak_copy: bytes must be a non-negative multiple of 16");
+    if (bytes > kMaxBytes) return fail(ATTN_ERR_TOO_LARGE, "attn_peak_copy: bytes too large");
+    int st;
+    if ((st = check_aligned(src, 16, "src must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(dst, 16, "dst must be 16-byte aligned")) != ATTN_OK) return st;
+    const Span outs[1] = {{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)bytes, "dst"}};
+    const Span ins[1] = {{(uintptr_t)src, (uintptr_t)src + (uintptr_t)bytes, "src"}};
+    if ((st = check_disjoint(outs, 1, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_peak_copy(src, dst, bytes, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_peak_copy launch");
+}
+
+int attn_peak_read_slots(void) { return cattn::peak_read_slots(); }
+
+int attn_peak_read(const void* src, long long bytes, unsigned int* out, void* stream) {
+    g_last_error[0] = '\0';
+    if (bytes == 0) return ATTN_OK;
+    if (!src || !out) return fail(ATTN_ERR_NULL_PTR, "attn_peak_read: src or out is NULL");
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_peak_read: bytes must be a non-negative multiple of 16");
+    if (bytes > kMaxBytes) return fail(ATTN_ERR_TOO_LARGE, "attn_peak_read: bytes too large");
+    int st;
+    if ((st = check_aligned(src, 16, "src must be 16-byte aligned")) != ATTN_OK) return st;
+    if ((st = check_aligned(out, 4, "out must be 4-byte aligned")) != ATTN_OK) return st;
+    const Span outs[1] = {{(uintptr_t)out, (uintptr_t)(out + cattn::peak_read_slots()), "out"}};
+    const Span ins[1] = {{(uintptr_t)src, (uintptr_t)src + (uintptr_t)bytes, "src"}};
+    if ((st = check_disjoint(outs, 1, ins, 1)) != ATTN_OK) return st;
+    const hipError_t e = cattn::launch_peak_read(src, bytes, out, as_stream(stream));
+    return e == hipSuccess ? ATTN_OK : fail_hip(e, "attn_peak_read launch");
+}
 
 }  // extern "C"

@@ -297,6 +297,37 @@ int attn_quantize_bwd_fp8(const void* dout, const void* qkv, const void* out, co
 int attn_bwd_fp8(const void* fp8, const void* fp8_bwd, void* dqkv, int B, int T, int n_head,
                  int head_dim, void* stream);
 
+/* -------------------------------------------------------- measurement ---- */
+
+/* Probes of the two rates the kernels are priced against, measured on the
+ * GPU the library runs on; not part of the attention path. They read the
+ * chip's sustained rates under load next to its specification (dense bf16
+ * MFMA 2516.6 TFLOP/s, HBM3E 8 TB/s).
+ *
+ * attn_peak_mfma: n_wg workgroups of four waves; each wave runs `iters`
+ * rounds of eight independent bf16 32x32x16 MFMAs on register operands
+ * (attn_peak_mfma_flops(n_wg, iters) FLOPs in all, -1 for arguments out of
+ * range). out: n_wg * 256 floats of the accumulators' sums (meaningless
+ * values that keep the work live); ticks: 2 * n_wg int64, the core-clock
+ * ticks (s_memtime) and 100 MHz constant-clock ticks (s_memrealtime) of each
+ * workgroup's first wave over its loop, whose ratio gives the clock the
+ * MFMAs ran at. n_wg and iters lie in [1, 2^20] (else ATTN_ERR_BAD_SHAPE);
+ * out 4-byte and ticks 8-byte aligned, not overlapping.
+ *
+ * attn_peak_copy: copies `bytes` (a multiple of 16) from src to dst with
+ * 16-byte nontemporal loads and stores; both 16-byte aligned, not
+ * overlapping. bytes = 0 does nothing. Errors as for the attention calls.
+ *
+ * attn_peak_read: reads `bytes` (a multiple of 16) from src with 16-byte
+ * loads; out (4-byte aligned, attn_peak_read_slots() uint32, not overlapping
+ * src) receives one XOR of the data per workgroup, which keeps the loads
+ * live. bytes = 0 does nothing. */
+long long attn_peak_mfma_flops(int n_wg, int iters);
+int attn_peak_mfma(float* out, long long* ticks, int n_wg, int iters, void* stream);
+int attn_peak_copy(const void* src, void* dst, long long bytes, void* stream);
+int attn_peak_read_slots(void);
+int attn_peak_read(const void* src, long long bytes, unsigned int* out, void* stream);
+
 /* ------------------------------------------------------------- status ---- */
 
 /* Static, human-readable name of a status code (never NULL). */

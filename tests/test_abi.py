@@ -49,6 +49,8 @@ def test_header_declares_expected_entry_points():
               "attn_fp8_buffer_bytes", "attn_quantize_fp8", "attn_fwd_fp8",
               "attn_block_fwd", "attn_block_bwd", "attn_block_workspace_bytes",
               "attn_fp8_bwd_buffer_bytes", "attn_quantize_bwd_fp8", "attn_bwd_fp8",
+              "attn_peak_mfma_flops", "attn_peak_mfma", "attn_peak_copy", "attn_peak_read",
+              "attn_peak_read_slots",
               "attn_status_string", "attn_last_error", "attn_version"):
         assert n in names
 
@@ -334,3 +336,36 @@ def test_binding_argument_checks_on_cpu_tensors():
         binding.forward(torch.zeros(1, 4, 100, dtype=torch.bfloat16), n_head=1)
     with pytest.raises(ValueError):
         binding.forward(torch.zeros(1, 4, 192, dtype=torch.float16), n_head=1)
+
+
+def test_peak_mfma_flops(L):
+    # 4 waves x iters x 8 MFMAs x (32 x 32 x 16 x 2) FLOPs per workgroup
+    assert L.attn_peak_mfma_flops(1, 1) == 4 * 8 * 32768
+    assert L.attn_peak_mfma_flops(2048, 4096) == 2048 * 4 * 4096 * 8 * 32768
+    for bad in ((0, 1), (1, 0), (-1, 5), (2**20 + 1, 1), (1, 2**20 + 1)):
+        assert L.attn_peak_mfma_flops(*bad) == -1, bad
+
+
+@no_gpu_only
+def test_peak_probe_validation(L):
+    assert L.attn_peak_mfma(None, DL, 4, 4, None) == -1
+    assert L.attn_peak_mfma(O, None, 4, 4, None) == -1
+    assert L.attn_peak_mfma(O, DL, 0, 4, None) == -2
+    assert L.attn_peak_mfma(O, DL, 4, 2**20 + 1, None) == -2
+    assert L.attn_peak_mfma(O + 2, DL, 4, 4, None) == -5
+    assert L.attn_peak_mfma(O, DL + 4, 4, 4, None) == -5
+    assert L.attn_peak_mfma(O, O + 1024, 4, 4, None) == -6   # ticks inside out
+    assert L.attn_peak_copy(Q, O, 0, None) == 0                # nothing to copy
+    assert L.attn_peak_copy(None, O, 64, None) == -1
+    assert L.attn_peak_copy(Q, O, 24, None) == -2              # not a multiple of 16
+    assert L.attn_peak_copy(Q, O, -16, None) == -2
+    assert L.attn_peak_copy(Q + 8, O, 64, None) == -5
+    assert L.attn_peak_copy(Q, Q + 32, 64, None) == -6         # dst overlaps src
+    assert L.attn_peak_read_slots() == 8192
+    assert L.attn_peak_read(Q, 0, None, None) == 0              # nothing to read
+    assert L.attn_peak_read(None, 64, O, None) == -1
+    assert L.attn_peak_read(Q, 64, None, None) == -1
+    assert L.attn_peak_read(Q, 40, O, None) == -2
+    assert L.attn_peak_read(Q + 4, 64, O, None) == -5
+    assert L.attn_peak_read(Q, 64, O + 2, None) == -5
+    assert L.attn_peak_read(Q, 1 << 20, Q + 64, None) == -6     # out inside src
