@@ -5,11 +5,12 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 A step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: attn_fwd then attn_bwd, on one HIP stream. W untimed
 steps, then K timed steps between two device synchronisations (HIP events on
-that stream bracket the K steps). A second timed pass of K steps launches the
-same kernels through the backward's two stage entry points
-(attn_bwd_dq_preprocess then attn_bwd_dkdv: exactly what attn_bwd launches)
-with HIP events recorded on the stream between them, which gives each
-kernel's average duration without slowing the first pass.
+that stream bracket the K steps). A second timed pass launches each kernel
+of the step K times back to back between two HIP events, in five blocks
+interleaved across the kernels, through attn_fwd and the backward's two
+stage entry points (attn_bwd_dq_preprocess then attn_bwd_dkdv: exactly what
+attn_bwd launches), which gives each kernel's average duration without
+slowing the first pass.
 
 Prints one JSON line. ``value`` is the counted causal FLOP rate of the whole
 step (forward 2*B*H*T^2*d, backward 2.5 times that); ``roofline`` describes
@@ -89,6 +90,8 @@ def parse_args(argv=None):
     p.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 forward")
     p.add_argument("--no-block", action="store_true", help="skip timing the attention layer")
     p.add_argument("--no-b64", action="store_true", help="skip the step at batch 64")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the steps after a cache-clearing scratch write")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA and HBM peak probes")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -195,14 +198,30 @@ def write_profiles(args, w) -> int:
     cmd = args.profile_command or "(see the bench.py --write-profiles invocation)"
     if args.trace_dir:
         rows = _csv_rows(args.trace_dir, "kernel_stats.csv")
+        trace = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                        for r in _csv_rows(args.trace_dir, "kernel_trace.csv")))
+        per, b2b = {}, {}  # name -> dispatch durations (us): all, and back to back
+        for i, (t0, t1, name) in enumerate(trace):
+            dur = (t1 - t0) / 1e3
+            per.setdefault(name, []).append(dur)
+            if ((i > 0 and trace[i - 1][2] == name) or
+                    (i + 1 < len(trace) and trace[i + 1][2] == name)):
+                b2b.setdefault(name, []).append(dur)
         lines = [f"# rocprofv3 kernel-trace statistics, workload {w.name}",
                  f"# command: {cmd}",
-                 "# kernel, calls, average_us, min_us, max_us, share_percent"]
+                 "# back_to_back_avg_us: mean over the dispatches that directly follow or precede "
+                 "a dispatch of the same kernel (bench.py's per-kernel pass, the regime of its "
+                 "kernels_us and roofline)",
+                 "# kernel, calls, average_us, median_us, min_us, max_us, share_percent, "
+                 "back_to_back_calls, back_to_back_avg_us"]
         for r in rows:
             k = _kernel_of(r["Name"]) or r["Name"][:60]
-            lines.append(f"{k}, {r['Calls']}, {float(r['AverageNs']) / 1e3:.2f}, "
+            med = statistics.median(per[r["Name"]]) if per.get(r["Name"]) else float("nan")
+            bb = b2b.get(r["Name"], [])
+            bb_avg = f"{sum(bb) / len(bb):.2f}" if bb else "-"
+            lines.append(f"{k}, {r['Calls']}, {float(r['AverageNs']) / 1e3:.2f}, {med:.2f}, "
                          f"{float(r['MinNs']) / 1e3:.2f}, {float(r['MaxNs']) / 1e3:.2f}, "
-                         f"{float(r['Percentage']):.2f}")
+                         f"{float(r['Percentage']):.2f}, {len(bb)}, {bb_avg}")
         path = os.path.join(PROFILE_DIR, f"kernel_stats_{w.name}.txt")
         with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")
@@ -687,14 +706,13 @@ def main(argv=None):
         binding.attn_fwd(qkv, out, lse, H, D, stream)
         binding.attn_bwd(dout, qkv, out, lse, dqkv, delta, H, D, stream)
 
-    def staged_step(evs):
-        evs[0].record(stream)
-        binding.attn_fwd(qkv, out, lse, H, D, stream)
-        evs[1].record(stream)
-        binding.attn_bwd_dq_preprocess(dout, qkv, out, lse, dqkv, delta, H, D, stream)
-        evs[2].record(stream)
-        binding.attn_bwd_dkdv(dout, qkv, delta, dqkv, H, D, stream)
-        evs[3].record(stream)
+    # The step's kernels one by one, through the stage entry points (exactly
+    # what attn_fwd and attn_bwd launch); each call is idempotent.
+    stages = {"attn_fwd": lambda: binding.attn_fwd(qkv, out, lse, H, D, stream),
+              "attn_bwd_dq_preprocess": lambda: binding.attn_bwd_dq_preprocess(
+                  dout, qkv, out, lse, dqkv, delta, H, D, stream),
+              "attn_bwd_dkdv": lambda: binding.attn_bwd_dkdv(dout, qkv, delta, dqkv, H, D, stream)}
+    assert list(stages) == STAGES
 
     for _ in range(args.warmup):
         step()
@@ -714,20 +732,31 @@ def main(argv=None):
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / K
 
-    # Kernel-timing region: K more steps with events between the kernels.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
-          for _ in range(K)]
+    # Kernel-timing region: each kernel of the step K times back to back
+    # between two HIP events on the step's stream, in 5 blocks of K/5 with the
+    # kernels interleaved block by block; the mean over all K launches and
+    # the median over the blocks. (Events recorded between the kernels of
+    # every step slow the kernels themselves by up to 10%, as rocprofv3's
+    # per-dispatch durations show, so they are not used.)
+    n_blk = 5
+    per_blk = max(1, K // n_blk)
+    blk_us = {name: [] for name in STAGES}
     torch.cuda.synchronize()
-    for i in range(K):
-        staged_step(ev[i])
-    torch.cuda.synchronize()
-    kernel_us = {}
-    for j, name in enumerate(STAGES):
-        kernel_us[name] = 1000.0 * sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
-    split_us = {"fwd": statistics.median(1000.0 * e[0].elapsed_time(e[1]) for e in ev),
-                "bwd": statistics.median(1000.0 * e[1].elapsed_time(e[-1]) for e in ev),
-                "step": statistics.median(1000.0 * e[0].elapsed_time(e[-1]) for e in ev)}
-    cold = time_cold(step, stream, dev, min(K, 20))
+    for _ in range(n_blk):
+        for name, fn in stages.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(per_blk):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            blk_us[name].append(1000.0 * e0.elapsed_time(e1) / per_blk)
+    kernel_us = {name: sum(v) / len(v) for name, v in blk_us.items()}
+    split_us = {"fwd": statistics.median(blk_us["attn_fwd"]),
+                "bwd": statistics.median(a + b for a, b in zip(blk_us["attn_bwd_dq_preprocess"],
+                                                               blk_us["attn_bwd_dkdv"])),
+                "kernels_sum": sum(statistics.median(v) for v in blk_us.values())}
+    cold = None if args.no_cold else time_cold(step, stream, dev, min(K, 20))
 
     flops = w.counted_flops()
     tflops = flops["total"] / (ms_per_step * 1e-3) / 1e12
@@ -794,11 +823,12 @@ def main(argv=None):
         "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "kernels_us": kernel_us,
         "split_us": split_us,
-        "cold": cold,
         "hbm": hbm,
         "host_wall_s": wall,
         "roofline": roof,
     }
+    if cold is not None:
+        result["cold"] = cold
     if peaks is not None:
         result["peaks"] = peaks
         result["pct_of_measured_bf16_peak"] = 100.0 * tflops / peaks["mfma_bf16_tflops"]

@@ -166,15 +166,25 @@ __device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, lds_bf16* t
                                          const int (&roff)[4], bf16x8 bs, bf16x8 bd, int toff,
                                          f32x16& s, f32x16& dp) {
     typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    // All nine operand reads first, then the MFMAs: the scheduling barrier
+    // keeps the compiler from pairing each read with the MFMA that uses it,
+    // which would expose one LDS latency per MFMA at the start of each half.
+    bf16x8 qa[4], ga[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int o = QB * 32 * 64 + roff[kk];
+        qa[kk] = *reinterpret_cast<lds_bf16x8*>(qt + o);
+        ga[kk] = *reinterpret_cast<lds_bf16x8*>(gt + o);
+    }
+    const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(terms + QB * 32 * 16 + toff);
+    __builtin_amdgcn_sched_barrier(0);
     s = zero16();
     dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const int o = QB * 32 * 64 + roff[kk];
-        s = mfma32(*reinterpret_cast<lds_bf16x8*>(qt + o), kreg[kk], s);
-        dp = mfma32(*reinterpret_cast<lds_bf16x8*>(gt + o), vreg[kk], dp);
+        s = mfma32(qa[kk], kreg[kk], s);
+        dp = mfma32(ga[kk], vreg[kk], dp);
     }
-    const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(terms + QB * 32 * 16 + toff);
     s = mfma32(a, bs, s);
     dp = mfma32(a, bd, dp);
 }
@@ -204,12 +214,22 @@ template <int QB>
 __device__ __forceinline__ void dkdv_acc(lds_bf16* qt, lds_bf16* gt, const int (&troff)[2][2],
                                          const bf16x8 (&pds)[4], f32x16 (&dvt)[2],
                                          f32x16 (&dkt)[2]) {
+    // The eight transposed operands first, then the MFMAs (as for S and dP).
+    bf16x8 ga[2][2], qa[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            ga[db][j] = atile_tr(gt, troff[db][0], troff[db][1], 2 * QB + j);
+            qa[db][j] = atile_tr(qt, troff[db][0], troff[db][1], 2 * QB + j);
+        }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB), pds[0], dvt[db]);
-        dvt[db] = mfma32(atile_tr(gt, troff[db][0], troff[db][1], 2 * QB + 1), pds[1], dvt[db]);
-        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB), pds[2], dkt[db]);
-        dkt[db] = mfma32(atile_tr(qt, troff[db][0], troff[db][1], 2 * QB + 1), pds[3], dkt[db]);
+        dvt[db] = mfma32(ga[db][0], pds[0], dvt[db]);
+        dvt[db] = mfma32(ga[db][1], pds[1], dvt[db]);
+        dkt[db] = mfma32(qa[db][0], pds[2], dkt[db]);
+        dkt[db] = mfma32(qa[db][1], pds[3], dkt[db]);
     }
 }
 
