@@ -18,8 +18,8 @@
 // reads as dO). Weights are stored (in, out).
 //
 // The weight gradients are long contractions (K = B * T) with small outputs,
-// so they run split over K into fp32 slabs that a second kernel adds in a
-// fixed order; the bias gradients are column sums done the same way. No
+// so they run split over K (as many splits as fill one round of workgroups)
+// into fp32 slabs that a second kernel adds in a fixed order; the bias gradients are column sums done the same way. No
 // atomics: the backward is deterministic.
 #include "attn_common.h"
 
@@ -28,6 +28,8 @@ namespace cattn {
 hipError_t launch_gemm_bf16(bool a_tr, bool b_tr, bool out_f32, const void* A, long long lda,
                             const void* B, long long ldb, void* C, long long ldc, const void* bias,
                             int M, int N, int K, int splits, hipStream_t stream);
+int gemm_tile_n(int N);
+int gemm_split_count(int K, int splits, int* chunk);
 hipError_t launch_attn_fwd_bf16(const void*, void*, float*, int, int, int, hipStream_t);
 hipError_t launch_attn_bwd_dq_pre_bf16(const void*, const void*, const void*, const float*, float*,
                                        void*, int, int, int, hipStream_t);
@@ -114,22 +116,31 @@ hipError_t colsum(const bf16* X, long long ld, int R, int N, float* parts, float
 
 }  // namespace
 
-// K splits of a weight-gradient product over R = B * T rows: as many as keep
-// about 1024 workgroups busy for an M x N output of 128 x 128 tiles, each
-// split a whole number of 64-row steps (1 when R is not a multiple of 64).
+// K splits asked of a weight-gradient product over R = B * T rows: as many
+// as make one full round of workgroups (two per CU on 256 CUs) for the
+// product's tiles, at most 64 and no more than one per four 64-row steps.
+// The fp32 slabs then number slabs_of(R, splits).
+constexpr int ROUND_WGS = 512;
+
 int block_splits(long long R, int M, int N) {
-    const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
-    int s = 1;
-    while (s < 64 && tiles * s * 2 <= 1024 && R % (64LL * s * 2) == 0) s *= 2;
-    return s;
+    const long long tiles = (long long)((M + 127) / 128) * ((N + gemm_tile_n(N) - 1) / gemm_tile_n(N));
+    long long s = ROUND_WGS / tiles;
+    if (s > 64) s = 64;
+    if (s > R / 256) s = R / 256;
+    return s < 1 ? 1 : (int)s;
+}
+
+int slabs_of(long long R, int splits) {
+    int chunk = 0;
+    return gemm_split_count((int)R, splits, &chunk);
 }
 
 long long block_workspace_floats(int B, int T, int H) {
     const long long C = (long long)H * HEAD_DIM, R = (long long)B * T;
     const long long tp = ((long long)T + 63) / 64 * 64;
     const long long delta = 10LL * B * H * tp;
-    const long long s_attn = block_splits(R, (int)C, (int)(3 * C));
-    const long long s_proj = block_splits(R, (int)C, (int)C);
+    const long long s_attn = slabs_of(R, block_splits(R, (int)C, (int)(3 * C)));
+    const long long s_proj = slabs_of(R, block_splits(R, (int)C, (int)C));
     long long parts = s_attn * C * 3 * C;
     if (s_proj * C * C > parts) parts = s_proj * C * C;
     const long long cs = (R + COLSUM_ROWS - 1) / COLSUM_ROWS * 3 * C;
@@ -166,9 +177,9 @@ hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void*
     hipError_t e = launch_gemm_bf16(false, false, false, dy, C, w_proj, C, datt, C, nullptr, R,
                                     (int)C, (int)C, 1, stream);
     if (e != hipSuccess) return e;
-    const int sp = block_splits(R, (int)C, (int)C);
+    const int sp_ask = block_splits(R, (int)C, (int)C), sp = slabs_of(R, sp_ask);
     if ((e = launch_gemm_bf16(true, true, true, att, C, dy, C, sp > 1 ? parts : dw_proj, C,
-                              nullptr, (int)C, (int)C, R / sp, sp, stream)) != hipSuccess)
+                              nullptr, (int)C, (int)C, R, sp_ask, stream)) != hipSuccess)
         return e;
     if (sp > 1) {
         hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((C * C + 255) / 256)), dim3(256), 0,
@@ -188,9 +199,9 @@ hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void*
     if ((e = launch_gemm_bf16(false, false, false, dqkv, 3 * C, w_attn, 3 * C, dx, C, nullptr, R,
                               (int)C, (int)(3 * C), 1, stream)) != hipSuccess)
         return e;
-    const int sa = block_splits(R, (int)C, (int)(3 * C));
+    const int sa_ask = block_splits(R, (int)C, (int)(3 * C)), sa = slabs_of(R, sa_ask);
     if ((e = launch_gemm_bf16(true, true, true, x, C, dqkv, 3 * C, sa > 1 ? parts : dw_attn,
-                              3 * C, nullptr, (int)C, (int)(3 * C), R / sa, sa, stream)) !=
+                              3 * C, nullptr, (int)C, (int)(3 * C), R, sa_ask, stream)) !=
         hipSuccess)
         return e;
     if (sa > 1) {

@@ -53,6 +53,7 @@ struct Output {
 struct GemmShape {
     int M, N, K, H;
     float alpha;
+    int K_tail;  // K of the batches with h = H - 1 (a shorter last K split); K elsewhere
 };
 
 // Descriptor over a 64 x 64 tile whose first element is at `p`, with `rows`
@@ -89,20 +90,23 @@ __device__ __forceinline__ void gemm_tr_offsets(int lane, int db, int* off0, int
     *off1 = r1 * 64 + (((d >> 3) ^ swz(r1)) << 3) + (d & 7);
 }
 
-// C[M x N] = alpha * A[M x K] B[K x N] per head; BN = 128 (waves 2 x 2, each
-// 64 x 64) or 64 (waves 4 x 1, each 32 x 64). Blocks: x = output tile,
-// y = (b, h). Two LDS stages.
+// C[M x N] = alpha * A[M x K] B[K x N] per head; BN = 192 (waves 2 x 2, each
+// 64 x 96), 128 (waves 2 x 2, each 64 x 64) or 64 (waves 4 x 1, each
+// 32 x 64). Blocks: x = output tile, y = (b, h). Two LDS stages (80 KB at
+// BN = 192, so that two workgroups fill a CU's LDS).
 template <int OPA, int OPB, int BN, bool OUT_F32>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Output Cout,
                                                         GemmShape g) {
     constexpr int NB_A = 2, NB_B = BN / 64;  // 64 x 64 tiles per stage
-    constexpr int WM = BN == 128 ? 2 : 1;    // 32-row MFMA blocks per wave
+    constexpr int WM = BN >= 128 ? 2 : 1;    // 32-row MFMA blocks per wave
+    constexpr int WN = BN == 192 ? 3 : 2;    // 32-column MFMA blocks per wave
     __shared__ bf16 sA[2][NB_A][ATILE_ELEMS];
     __shared__ bf16 sB[2][NB_B][ATILE_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
 
     const int bh = blockIdx.y, b = bh / g.H, h = bh - b * g.H;
+    const int K = h == g.H - 1 ? g.K_tail : g.K;
     const int tiles_n = (g.N + BN - 1) / BN;
     const int m0 = (blockIdx.x / tiles_n) * G_BM, n0 = (blockIdx.x % tiles_n) * BN;
     const bf16* Ab = A.base + b * A.stride_b + h * A.stride_h;
@@ -110,9 +114,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
     const TileLoader la = tile_loader(A.ld, wave, lane);
     const TileLoader lb = tile_loader(B.ld, wave, lane);
 
-    // Wave's output block: rows wm0 .. wm0 + 32 WM - 1, columns wn0 .. wn0 + 63.
-    const int wm0 = BN == 128 ? (wave & 1) * 64 : wave * 32;
-    const int wn0 = BN == 128 ? (wave >> 1) * 64 : 0;
+    // Wave's output block: rows wm0 .. wm0 + 32 WM - 1, columns wn0 .. wn0 + 32 WN - 1.
+    const int wm0 = BN >= 128 ? (wave & 1) * 64 : wave * 32;
+    const int wn0 = BN >= 128 ? (wave >> 1) * 32 * WN : 0;
     int troff[2][2];
 #pragma unroll
     for (int db = 0; db < 2; ++db) gemm_tr_offsets(lane, db, &troff[db][0], &troff[db][1]);
@@ -124,8 +128,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
                     int n_outer, int t, int k0, bf16* dst) {
         const int o = outer0 + 64 * t;
         i32x4 r;
-        if (op == OP_ROW) r = tile_rsrc(base + (long long)o * ld + k0, ld, n_outer - o, g.K - k0);
-        else r = tile_rsrc(base + (long long)k0 * ld + o, ld, g.K - k0, n_outer - o);
+        if (op == OP_ROW) r = tile_rsrc(base + (long long)o * ld + k0, ld, n_outer - o, K - k0);
+        else r = tile_rsrc(base + (long long)k0 * ld + o, ld, K - k0, n_outer - o);
         atile_load(atile_addr(dst), r, 0, L);
     };
     auto issue = [&](int ks, int st) {
@@ -143,11 +147,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
         return atile_tr(tile, troff[part][0], troff[part][1], kc);
     };
 
-    f32x16 acc[WM][2];
+    f32x16 acc[WM][WN];
 #pragma unroll
-    for (int i = 0; i < WM; ++i) acc[i][0] = acc[i][1] = zero16();
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = zero16();
 
-    const int n_k = (g.K + G_BK - 1) / G_BK;
+    const int n_k = (K + G_BK - 1) / G_BK;
     issue(0, 0);
     for (int ks = 0; ks < n_k; ++ks) {
         wait_vmem<0>();
@@ -156,14 +162,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
         const int st = ks & 1;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            bf16x8 bop[2];
+            bf16x8 bop[WN];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) bop[nb] = operand(OPB, sB[st][0], (wn0 >> 5) + nb, kc);
+            for (int nb = 0; nb < WN; ++nb) bop[nb] = operand(OPB, sB[st][0], (wn0 >> 5) + nb, kc);
 #pragma unroll
             for (int mb = 0; mb < WM; ++mb) {
                 const bf16x8 aop = operand(OPA, sA[st][0], (wm0 >> 5) + mb, kc);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(aop, bop[nb], acc[mb][nb]);
+                for (int nb = 0; nb < WN; ++nb) acc[mb][nb] = mfma32(aop, bop[nb], acc[mb][nb]);
             }
         }
     }
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Operand A, Operand B, Ou
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < WN; ++nb) {
             const int n = n0 + wn0 + nb * 32 + l32;
             if (n >= g.N) continue;
             const float bias = Cout.bias ? (float)Cout.bias[n] : 0.0f;
@@ -312,9 +318,9 @@ hipError_t launch_softmax_bwd(const bf16* P, const float* dP, bf16* dS, int Tp8,
 
 template <int OPA, int OPB, int BN, bool OUT_F32>
 hipError_t gemm(Operand A, Operand B, Output C, int M, int N, int K, int BH, int H, float alpha,
-                hipStream_t stream) {
+                hipStream_t stream, int K_tail = -1) {
     const long long tiles = (long long)((M + G_BM - 1) / G_BM) * ((N + BN - 1) / BN);
-    const GemmShape g{M, N, K, H, alpha};
+    const GemmShape g{M, N, K, H, alpha, K_tail < 0 ? K : K_tail};
     hipLaunchKernelGGL((gemm_bf16_kernel<OPA, OPB, BN, OUT_F32>), dim3((unsigned)tiles, (unsigned)BH),
                        dim3(256), 0, stream, A, B, C, g);
     return hipGetLastError();
@@ -322,26 +328,60 @@ hipError_t gemm(Operand A, Operand B, Output C, int M, int N, int K, int BH, int
 
 }  // namespace
 
+// Column tile of the layer products: 192 where N allows, else 128. At
+// N = 768 the 128 x 192 tiles make 512 tiles per 16384 rows, one full round
+// of two workgroups per CU, where 128 x 128 tiles leave the second round half
+// empty.
+int gemm_tile_n(int N) { return N % 192 == 0 ? 192 : 128; }
+
+// K splits of a split product: chunks of round_up(ceil(K / splits), 64)
+// elements, the last one shorter; returns how many chunks that makes (at most
+// `splits`) and their length.
+int gemm_split_count(int K, int splits, int* chunk) {
+    if (splits <= 1 || K <= 64) {
+        *chunk = K;
+        return 1;
+    }
+    const int c = ((K + splits - 1) / splits + 63) / 64 * 64;
+    *chunk = c;
+    return (K + c - 1) / c;
+}
+
 // One plain (un-batched) product C = A B (+ bias per column) for the linear
-// maps around the attention, or `splits` independent products over
-// consecutive K ranges (split_k elements each) into consecutive M x N fp32
-// slabs. A is M x K, stored k-contiguous (a_tr false, row stride lda) or
-// m-contiguous (a_tr true: element (m, k) at k * lda + m); B is K x N, stored
-// n-contiguous (b_tr true: element (k, n) at k * ldb + n) or k-contiguous
-// (b_tr false: element (k, n) at n * ldb + k). C has row stride ldc.
+// maps around the attention, or a split product: the K range cut as
+// gemm_split_count says, chunk s into the s-th consecutive M x N fp32 slab.
+// A is M x K, stored k-contiguous (a_tr false, row stride lda) or
+// M-contiguous (a_tr true: element (m, k) at k * lda + m); B is K x N, stored
+// N-contiguous (b_tr true: element (k, n) at k * ldb + n) or k-contiguous
+// (b_tr false: element (k, n) at n * ldb + k). C is M x N row-major (ldc).
+// Strides and column offsets are multiples of 8 elements (16 bytes). The
+// orientations the layer uses: (A row, B tr) for x W and att W_proj, (A row,
+// B row) for dy W_proj^T and dqkv W_attn^T, and (A tr, B tr) with fp32
+// output for the weight gradients.
 hipError_t launch_gemm_bf16(bool a_tr, bool b_tr, bool out_f32, const void* A_v, long long lda,
                             const void* B_v, long long ldb, void* C_v, long long ldc,
                             const void* bias, int M, int N, int K, int splits,
                             hipStream_t stream) {
     const bf16* A_p = static_cast<const bf16*>(A_v);
     const bf16* B_p = static_cast<const bf16*>(B_v);
-    // a K chunk of split k starts K * k elements along k
-    const long long a_step = a_tr ? (long long)K * lda : K, b_step = b_tr ? (long long)K * ldb : K;
+    int chunk = K;
+    const int n_split = gemm_split_count(K, splits, &chunk);
+    const int K_tail = K - (n_split - 1) * chunk;
+    // chunk k of the split starts chunk * k elements along k
+    const long long a_step = a_tr ? (long long)chunk * lda : chunk;
+    const long long b_step = b_tr ? (long long)chunk * ldb : chunk;
     const Operand A{A_p, 0, a_step, lda}, B{B_p, 0, b_step, ldb};
     const Output C{C_v, 0, (long long)M * ldc, ldc, static_cast<const bf16*>(bias)};
-    if (!a_tr && b_tr && !out_f32) return gemm<OP_ROW, OP_TR, 128, false>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
-    if (!a_tr && !b_tr && !out_f32) return gemm<OP_ROW, OP_ROW, 128, false>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
-    if (a_tr && b_tr && out_f32) return gemm<OP_TR, OP_TR, 128, true>(A, B, C, M, N, K, splits, splits, 1.0f, stream);
+    const bool wide = gemm_tile_n(N) == 192;
+#define CATTN_GEMM(OA, OB, BN_, F32)                                                              \
+    gemm<OA, OB, BN_, F32>(A, B, C, M, N, chunk, n_split, n_split, 1.0f, stream, K_tail)
+    if (!a_tr && b_tr && !out_f32)
+        return wide ? CATTN_GEMM(OP_ROW, OP_TR, 192, false) : CATTN_GEMM(OP_ROW, OP_TR, 128, false);
+    if (!a_tr && !b_tr && !out_f32)
+        return wide ? CATTN_GEMM(OP_ROW, OP_ROW, 192, false) : CATTN_GEMM(OP_ROW, OP_ROW, 128, false);
+    if (a_tr && b_tr && out_f32)
+        return wide ? CATTN_GEMM(OP_TR, OP_TR, 192, true) : CATTN_GEMM(OP_TR, OP_TR, 128, true);
+#undef CATTN_GEMM
     return hipErrorInvalidValue;  // orientation not used by the library
 }
 
