@@ -83,17 +83,20 @@ bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi;
 // Shape checks shared by every entry point. Sets *empty when there is
 // nothing to compute.
 constexpr long long kMaxChannels = 1LL << 23;  // 64 rows * 3C * 2 bytes < 2^32
+constexpr int kMaxT = 1 << 30;
 
 int check_shape(int B, int T, int H, int d, int elem, bool* empty) {
     if (B < 0 || T < 0 || H < 0 || d <= 0) return fail(ATTN_ERR_BAD_SHAPE, "B, T, n_head must be >= 0 and head_dim > 0");
     if (d != kHeadDim) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64");
     *empty = (B == 0 || T == 0 || H == 0);
     if (*empty) return ATTN_OK;
+    // Tile counts are rounded up from T in 32-bit arithmetic.
+    if (T > kMaxT) return fail(ATTN_ERR_TOO_LARGE, "T exceeds 2^30");
     // Largest tensor: qkv / dqkv with B*T*3*H*d elements; grid: B*H*ceil(T/64).
     const long long bt = (long long)B * T;
     const long long c3 = 3LL * H * d;
     if (bt > kMaxBytes / c3 / elem) return fail(ATTN_ERR_TOO_LARGE, "B*T*3*n_head*head_dim overflows");
-    const long long blocks = (long long)B * H * ((T + 63) / 64);
+    const long long blocks = (long long)B * H * (((long long)T + 63) / 64);
     if (blocks > kMaxBlocks) return fail(ATTN_ERR_TOO_LARGE, "launch grid exceeds 2^31-1 workgroups");
     // the preprocess grid: 16 rows of (b, t, h) per workgroup in float32, plus
     // one thread per padded workspace row entry
@@ -297,6 +300,15 @@ long long unfused_ws_bytes(int B, int T, int H) {
     return 6LL * B * H * T * cattn::unfused_row_stride(T);
 }
 
+// Size queries answer -1 for a negative argument and for a size past 2^62
+// bytes (which no call accepts); the bound is computed in 128 bits before any
+// 64-bit size arithmetic runs.
+typedef __int128 i128;
+
+bool past_limit(i128 bytes) { return bytes > (i128)kMaxBytes; }
+
+i128 round_up(i128 x, int m) { return (x + m - 1) / m * m; }
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +350,8 @@ int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqk
 
 long long attn_unfused_workspace_bytes(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    if (past_limit((i128)6 * B * n_head * T * round_up(T, 8))) return -1;
     return unfused_ws_bytes(B, T, n_head);
 }
 
@@ -396,6 +410,8 @@ int attn_bwd_unfused(const void* dout, const void* qkv, const void* probs, void*
 long long attn_decode_workspace_floats(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
     if (B == 0 || T == 0 || n_head == 0) return 0;
+    // at most one split per cache row, each of a few hundred bytes
+    if (past_limit((i128)B * n_head * T * 1024)) return -1;
     return cattn::decode_workspace_floats(B, T, n_head);
 }
 
@@ -444,6 +460,11 @@ int attn_decode(const void* q, long long q_batch_stride, const void* k_cache, co
 long long attn_block_workspace_bytes(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
     if (B == 0 || T == 0 || n_head == 0) return 0;
+    // beyond the shapes attn_block_bwd accepts (B * T <= 16776960 and
+    // n_head * 64 <= 2^23) the answer is -1
+    if ((long long)B * T > 65535LL * 256 || (long long)n_head * kHeadDim > kMaxChannels) return -1;
+    const i128 C = (i128)n_head * kHeadDim;
+    if (past_limit(4 * ((i128)10 * B * n_head * round_up(T, 64) + 64 * C * 3 * C))) return -1;
     return 4 * cattn::block_workspace_floats(B, T, n_head);
 }
 
@@ -520,6 +541,9 @@ int attn_block_bwd(const void* dy, const void* x, const void* w_attn, const void
 long long attn_fp8_bwd_buffer_bytes(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
     if (B == 0 || T == 0 || n_head == 0) return 0;
+    if (round_up(T, 64) * 64 > 0xffffffffLL) return -1;  // beyond the FP8 path's limit
+    // five 64-byte code rows plus 18 side bytes per padded position
+    if (past_limit((i128)B * n_head * round_up(T, 64) * 512)) return -1;
     return cattn::fp8_bwd_buffer_bytes(B, T, n_head);
 }
 
@@ -572,6 +596,9 @@ int attn_bwd_fp8(const void* fp8, const void* fp8_bwd, void* dqkv, int B, int T,
 long long attn_fp8_buffer_bytes(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
     if (B == 0 || T == 0 || n_head == 0) return 0;
+    if (round_up(T, 64) * 64 > 0xffffffffLL) return -1;  // beyond the FP8 path's limit
+    // three 64-byte code rows plus 6 exponent bytes per padded position
+    if (past_limit((i128)B * n_head * round_up(T, 64) * 512)) return -1;
     return cattn::fp8_buffer_bytes(B, T, n_head);
 }
 
@@ -618,6 +645,8 @@ int attn_fwd_fp8(const void* fp8, void* out, float* lse, int B, int T, int n_hea
 
 long long attn_bwd_workspace_floats(int B, int T, int n_head) {
     if (B < 0 || T < 0 || n_head < 0) return -1;
+    if (B == 0 || T == 0 || n_head == 0) return 0;
+    if (past_limit((i128)40 * B * n_head * round_up(T, 64))) return -1;
     return workspace_floats(B, T, n_head);
 }
 

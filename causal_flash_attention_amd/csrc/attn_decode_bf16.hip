@@ -124,10 +124,10 @@ __global__ __launch_bounds__(HEAD_DIM) void decode_combine_kernel(const float* w
 // Splits per head: enough workgroups to cover the chip (about 2048), each
 // with at least 64 keys.
 int decode_splits(int BH, int T) {
-    int n = (2048 + BH - 1) / BH;
-    const int max_n = (T + 63) / 64;
+    long long n = (2048LL + BH - 1) / (BH > 0 ? BH : 1);
+    const long long max_n = (T + 63LL) / 64;
     if (n > max_n) n = max_n;
-    return n < 1 ? 1 : n;
+    return n < 1 ? 1 : (int)n;
 }
 
 long long decode_workspace_floats(int B, int T, int H) {

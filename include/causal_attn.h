@@ -60,7 +60,7 @@
  * streams may run concurrently as long as their buffers do not overlap.
  *
  * Shapes: head_dim must be 64. B, T and n_head may be any non-negative value
- * with n_head * head_dim <= 2^23, whose tensors fit in 2^62 bytes and whose
+ * with T <= 2^30, n_head * head_dim <= 2^23, whose tensors fit in 2^62 bytes and whose
  * launch grids fit in 2^31 - 1 workgroups; a call with B, T or n_head equal to 0 has nothing to compute
  * and returns ATTN_OK without touching memory (its pointers may then be
  * NULL). qkv, out, dout, dqkv and delta must start on a 16-byte boundary,
@@ -126,7 +126,8 @@ int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqk
                 int B, int T, int n_head, int head_dim, void* stream);
 
 /* Number of floats the backward workspace `delta` must hold for this shape:
- * 2 * B * n_head * round_up(T, 64); -1 if an argument is negative. */
+ * 10 * B * n_head * round_up(T, 64). Like every size query here it returns
+ * -1 if an argument is negative or the size would pass 2^62 bytes. */
 long long attn_bwd_workspace_floats(int B, int T, int n_head);
 
 /* --------------------------------------------------------------- fp32 ---- */
@@ -218,7 +219,8 @@ int attn_decode(const void* q, long long q_batch_stride,
  * All launches go on `stream`; nothing is allocated. Matrices, weights and ws
  * must be 16-byte aligned, biases 2-byte, float32 gradients and lse 4-byte;
  * no output may overlap an input or another output. Extra limit:
- * B * T <= 16776960 (ATTN_ERR_TOO_LARGE). */
+ * B * T <= 16776960 (ATTN_ERR_TOO_LARGE); attn_block_workspace_bytes
+ * returns -1 beyond it, for n_head * 64 > 2^23 and for negative arguments. */
 long long attn_block_workspace_bytes(int B, int T, int n_head);
 int attn_block_fwd(const void* x, const void* w_attn, const void* b_attn, const void* w_proj,
                    const void* b_proj, void* qkv, void* att, float* lse, void* y, int B, int T,
@@ -263,6 +265,8 @@ int attn_block_bwd(const void* dy, const void* x, const void* w_attn, const void
  * sum their 64 exact products with about 14 significant bits (measured), so
  * the results differ from an exact evaluation of the definition where a
  * weight's argument lies within that error of an E4M3 rounding midpoint. */
+/* attn_fp8_buffer_bytes and attn_fp8_bwd_buffer_bytes return -1 for negative
+ * arguments and beyond the FP8 path's limit on T. */
 long long attn_fp8_buffer_bytes(int B, int T, int n_head);
 int attn_quantize_fp8(const void* qkv, void* fp8, int B, int T, int n_head, int head_dim,
                       void* stream);

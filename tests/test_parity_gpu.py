@@ -28,12 +28,21 @@ def _scale_qk(qkv, dtype, H, gain):
     return I.f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
+def _transform(qkv, dtype, fn):
+    """Apply fn to the float32 values of qkv, then round back to the dtype."""
+    x = I.bf16_bits_to_f32(qkv) if dtype == "bf16" else qkv.copy()
+    x = fn(x).astype(np.float32)
+    return I.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
 def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", qk_gain=1.0,
-                stress=False):
+                stress=False, transform=None):
     log(f"[case] {label} B={B} T={T} H={H} dtype={dtype} seed={seed} qk_gain={qk_gain}")
     qkv, dout = I.attention_inputs(B, T, H, D, dtype, qkv_std, dout_std, seed=seed)
     if qk_gain != 1.0:
         qkv = _scale_qk(qkv, dtype, H, qk_gain)
+    if transform is not None:
+        qkv = _transform(qkv, dtype, transform)
     q64, g64 = I.to_float64(qkv, dtype), I.to_float64(dout, dtype)
     qd, gd = to_device(qkv, dtype), to_device(dout, dtype)
     out, lse, dqkv = run_library(qd, gd, H)
@@ -96,3 +105,62 @@ def test_peaky_scores_bf16():
 
 def test_peaky_scores_f32():
     _check_case(1, 200, 2, "f32", 1.0, 1.0, seed=12, label="peaky", qk_gain=4.0)
+
+
+# ----------------------------------------------------------------------------
+# Inputs that drive the online softmax's rescale and the value range.
+# ----------------------------------------------------------------------------
+
+def _growing_keys(H, a=16.0, g=1.0 / 16.0):
+    """Q_i += a u and K_j += g j u with u = (1/8, ..., 1/8) (a unit vector for
+    d = 64), so the logit of key j grows by about a g / 8 = 1/8 per key: the
+    running row maximum rises by more than 12 (base 2) on every 64-key tile,
+    above the forward's lazy-rescale threshold of 8, so every tile of every
+    row takes the rescale branch.
+
+    The ramp sits mostly on the query side on purpose. Each row of dS sums to
+    zero, so dQ_i = sum_j dS_ij (K_j - c) for any c, and the bf16 rounding of
+    dS (2^-9 per element) is amplified in dQ by |K| over the spread of K
+    where the row's softmax lives. A key ramp of g = 1/4 (|K| about 16 at
+    T = 512 against a spread near 1) gives a float64 emulation of that
+    rounding alone 1.5e-2 relative L2 on dQ, close to the bar; a = 16,
+    g = 1/16 gives 4.2e-3 (dK 1.5e-3, dV 1.7e-3)."""
+    C = H * D
+
+    def fn(x):
+        T = x.shape[1]
+        u = np.float32(1.0 / 8.0)
+        ramp = (g * np.arange(T, dtype=np.float32) * u)[None, :, None]
+        x[..., :C] += np.float32(a) * u
+        x[..., C:2 * C] += ramp
+        return x
+    return fn
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_growing_keys_rescale_every_tile(dtype):
+    dout_std = 0.01 if dtype == "bf16" else 1.0
+    _check_case(2, 512, 2, dtype, 1.0, dout_std, seed=21, label="growing keys", stress=True,
+                transform=_growing_keys(2))
+
+
+def _binade_edge_values(H):
+    """V replaced by +-m 2^e with m = 1 or 2 - 2^-7 (the two ends of a bf16
+    binade) and e from -24 to 60, chosen from the drawn value itself, so V
+    spans 85 binades and every sum of its rows crosses binade edges."""
+    C = H * D
+
+    def fn(x):
+        v = x[..., 2 * C:3 * C].astype(np.float64)
+        e = np.clip(np.round(12.0 * v) + 18.0, -24, 60)
+        m = np.where(np.abs(v) > 0.6745, 2.0 - 2.0 ** -7, 1.0)
+        x[..., 2 * C:3 * C] = (np.sign(v) * m * np.exp2(e)).astype(np.float32)
+        return x
+    return fn
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_values_at_binade_edges(dtype):
+    dout_std = 0.01 if dtype == "bf16" else 1.0
+    _check_case(1, 300, 2, dtype, 1.0, dout_std, seed=22, label="binade-edge V", stress=True,
+                transform=_binade_edge_values(2))
