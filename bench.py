@@ -104,6 +104,10 @@ def parse_args(argv=None):
     p.add_argument("--trace-dir", default=None)
     p.add_argument("--fetch-dir", default=None)
     p.add_argument("--write-dir", default=None)
+    p.add_argument("--mfma-dir", default=None,
+                   help="rocprofv3 --pmc output with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, "
+                        "SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE")
+    p.add_argument("--mfma-command", default="", help="the command that produced --mfma-dir")
     p.add_argument("--profile-command", default="",
                    help="the commands that produced the CSVs, recorded in the summaries")
     return p.parse_args(argv)
@@ -192,6 +196,44 @@ def _counter_means(d: str, counter: str):
     return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in per.items()}
 
 
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+N_XCD = 8
+
+
+def write_mfma_profile(args, w) -> None:
+    """MFMA utilisation per kernel from a counter pass: busy cycles summed
+    over all SIMDs over (GPU-active cycles of one XCD x SIMDs), the derived
+    MfmaUtil of rocprofv3, and the share of LDS-active cycles lost to bank
+    conflicts. GRBM_GUI_ACTIVE comes summed over the eight XCDs."""
+    per = {}
+    for r in _csv_rows(args.mfma_dir, "counter_collection.csv"):
+        k = _kernel_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# MFMA utilisation per kernel, workload {w.name}, from rocprofv3 counters",
+             f"# command: {args.mfma_command or '(see the bench.py --write-profiles invocation)'}",
+             "# mfma_util = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);",
+             "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; means over the dispatches",
+             "# kernel, dispatches, mfma_busy_cycles_per_simd, gui_active_cycles, mfma_util_percent, "
+             "lds_conflict_percent"]
+    order = list(KERNELS) + [k for k in sorted(per) if k not in KERNELS]
+    for k in order:
+        d = per.get(k)
+        if not d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        busy = statistics.mean(d["SQ_VALU_MFMA_BUSY_CYCLES"]) / N_SIMD
+        active = statistics.mean(d["GRBM_GUI_ACTIVE"]) / N_XCD
+        lds = statistics.mean(d.get("SQ_LDS_IDX_ACTIVE", [0.0]))
+        conf = statistics.mean(d.get("SQ_LDS_BANK_CONFLICT", [0.0]))
+        lines.append(f"{k}, {len(d['GRBM_GUI_ACTIVE'])}, {busy:.0f}, {active:.0f}, "
+                     f"{100.0 * busy / active:.1f}, {100.0 * conf / lds if lds else 0.0:.1f}")
+    path = os.path.join(PROFILE_DIR, f"mfma_util_{w.name}.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def write_profiles(args, w) -> int:
     """Turn rocprofv3 CSV output into the text summaries under profiles/."""
     os.makedirs(PROFILE_DIR, exist_ok=True)
@@ -226,6 +268,8 @@ def write_profiles(args, w) -> int:
         with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")
         print(path)
+    if args.mfma_dir:
+        write_mfma_profile(args, w)
     if args.fetch_dir and args.write_dir:
         fetch = _counter_means(args.fetch_dir, "FETCH_SIZE")
         write = _counter_means(args.write_dir, "WRITE_SIZE")
