@@ -71,10 +71,15 @@ __device__ __forceinline__ u32x4 mfma_terms_pad() {
     return v;
 }
 
-// Workspace row r's 32 bytes of MFMA terms: [m terms | D terms], m = 8 * LSE.
+// The MFMA terms of the workspace rows (m = 8 * LSE, and D), 16 bytes each,
+// in groups of 32 rows: the m terms of the group's 32 rows, then their D
+// terms, so that 16 lanes reading 16 consecutive rows' terms touch 256
+// consecutive bytes (no LDS bank conflict once the group is staged).
 __device__ __forceinline__ u32x4* ws_terms(float* ws, long long n_pad_rows) {
     return reinterpret_cast<u32x4*>(ws + 2 * n_pad_rows);
 }
+__device__ __forceinline__ long long term_m(long long r) { return (r >> 5) * 64 + (r & 31); }
+__device__ __forceinline__ long long term_d(long long r) { return term_m(r) + 32; }
 
 // Blocks [0, nb_d): D, two lanes per (b, t, h) row (one per half).
 // Blocks [nb_d, ...): one thread per padded (bh, t): LSE * log2 e and the m
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
             const int t = (int)(bt - b * T);
             const long long r = (b * H + h) * Tp + t;
             if (half == 0) dd[r] = acc;
-            else ws_terms(ws, n_pad_rows)[2 * r + 1] = mfma_terms(acc);
+            else ws_terms(ws, n_pad_rows)[term_d(r)] = mfma_terms(acc);
         }
     } else {
         const long long i = (blk - nb_d) * 256 + threadIdx.x;  // padded (bh, t)
@@ -119,12 +124,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
             if (t < T) {
                 const float l = lse[bh * T + t];
                 lse2[i] = l * LOG2E;
-                terms[2 * i] = mfma_terms(8.0f * l);
+                terms[term_m(i)] = mfma_terms(8.0f * l);
             } else {
                 lse2[i] = INFINITY;
                 dd[i] = 0.0f;
-                terms[2 * i] = mfma_terms_pad();
-                terms[2 * i + 1] = mfma_terms(0.0f);
+                terms[term_m(i)] = mfma_terms_pad();
+                terms[term_d(i)] = mfma_terms(0.0f);
             }
         }
     }
@@ -148,7 +153,7 @@ constexpr int KV_BM = 64;   // queries per LDS tile
 struct alignas(16) DkdvSmem {
     bf16 q[NSTAGE][ATILE_ELEMS];
     bf16 g[NSTAGE][ATILE_ELEMS];
-    bf16 terms[NSTAGE][KV_BM * 16];  // per query row: [m terms | D terms]
+    bf16 terms[NSTAGE][KV_BM * 16];  // two groups of 32 rows: 32 m terms, then 32 D terms
 };
 
 // The dK/dV step on a 64-query tile runs as two 32-query halves (QB), each
@@ -176,7 +181,7 @@ __device__ __forceinline__ void dkdv_sdp(lds_bf16* qt, lds_bf16* gt, lds_bf16* t
         qa[kk] = *reinterpret_cast<lds_bf16x8*>(qt + o);
         ga[kk] = *reinterpret_cast<lds_bf16x8*>(gt + o);
     }
-    const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(terms + QB * 32 * 16 + toff);
+    const bf16x8 a = *reinterpret_cast<lds_bf16x8*>(terms + QB * 512 + toff);
     __builtin_amdgcn_sched_barrier(0);
     s = zero16();
     dp = zero16();
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
 
     // Extra k-step operands: A = the row's terms (lane half 0: m, half 1: D),
     // read at toff; B = -1 on the first three k of the matching half.
-    const int toff = l32 * 16 + hf * 8;
+    const int toff = hf * 256 + l32 * 8;  // row l32's m (hf 0) or D (hf 1) terms
     const bf16 m1 = (bf16)-1.0f, z0 = (bf16)0.0f;
     const bf16x8 neg3 = {m1, m1, m1, z0, z0, z0, z0, z0}, zero8 = {z0, z0, z0, z0, z0, z0, z0, z0};
     const bf16x8 bs = hf == 0 ? neg3 : zero8;
@@ -561,8 +566,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
         ws[r] = dd;
         ws[(long long)BH * Tp + r] = lse2;
         u32x4* terms = ws_terms(ws, (long long)BH * Tp);
-        terms[2 * r] = q_ok ? mfma_terms(8.0f * lse[(long long)bh * T + my_q]) : mfma_terms_pad();
-        terms[2 * r + 1] = mfma_terms(dd);
+        terms[term_m(r)] = q_ok ? mfma_terms(8.0f * lse[(long long)bh * T + my_q]) : mfma_terms_pad();
+        terms[term_d(r)] = mfma_terms(dd);
     }
 
     if (q_ok) {

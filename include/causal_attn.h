@@ -39,9 +39,11 @@
  *                 row index r = (b * n_head + h) * Tp + t:
  *                   floats [0, R):   D[b, h, t] = sum_k dout * out (0 for t >= T)
  *                   floats [R, 2R):  LSE * log2(e) (+inf for t >= T)
- *                   bytes from 8R:   32 bytes per row, eight bf16 [m1 m2 m3 0 0 0
- *                                    0 0] then eight bf16 [d1 d2 d3 0 0 0 0 0],
- *                                    where m1 + m2 + m3 splits m = 8 * LSE and
+ *                   bytes from 8R:   32 bytes per row in groups of 32 rows
+ *                                    (1 KB each): the group's 32 m chunks,
+ *                                    eight bf16 [m1 m2 m3 0 0 0 0 0] each,
+ *                                    then its 32 D chunks [d1 d2 d3 0 0 0 0
+ *                                    0]; m1 + m2 + m3 splits m = 8 * LSE and
  *                                    d1 + d2 + d3 splits D into three bf16
  *                                    terms of decreasing size (for t >= T:
  *                                    m1 = the largest finite bf16, the rest 0)

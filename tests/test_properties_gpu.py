@@ -109,9 +109,11 @@ def test_stage_entry_points_match_attn_bwd():
     l_ref = lse.cpu().numpy().astype(np.float64) * np.log2(np.e)
     np.testing.assert_allclose(w[1, :, :, :T], l_ref, rtol=1e-6, atol=1e-6)
     assert np.all(np.isposinf(w[1, :, :, T:]))
-    # then 32 bytes per row: bf16 terms [m1 m2 m3 0 0 0 0 0 | d1 d2 d3 0 0 0 0 0]
+    # then 32 bytes per row in groups of 32 rows (the group's m chunks, then
+    # its D chunks): bf16 terms [m1 m2 m3 0 0 0 0 0] and [d1 d2 d3 0 0 0 0 0]
     # summing to m = 8 * LSE and to D; rows past T: m1 = largest finite bf16
-    bits = w_all[2 * R:].view(np.uint16).reshape(B, H, Tp, 2, 8)
+    grouped = w_all[2 * R:].view(np.uint16).reshape(B, H, Tp // 32, 2, 32, 8)
+    bits = grouped.transpose(0, 1, 2, 4, 3, 5).reshape(B, H, Tp, 2, 8)
     terms = I.bf16_bits_to_f32(bits).astype(np.float64)
     assert np.all(bits[..., 3:] == 0)
     m_sum = terms[:, :, :, 0, :3].sum(-1)
