@@ -28,7 +28,8 @@ how far its output lies from the bf16 forward's. ``split_us`` gives the
 median forward, backward and step times of the kernel-timing pass; ``cold``
 times single steps after a 512 MiB scratch write (inputs out of every
 cache); ``hbm`` is the step's algorithmic HBM rate; ``b64`` times the same
-step at batch 64; ``peaks`` measures the chip's sustained bf16 MFMA rate (and
+step at batch 64 and ``other_shapes`` at the 16-head and T = 2048 shapes;
+``peaks`` measures the chip's sustained bf16 MFMA rate (and
 the clock it ran at) and its HBM copy rate with the library's probes, next to
 the specification peaks the roofline uses.
 """
@@ -89,7 +90,8 @@ def parse_args(argv=None):
     p.add_argument("--no-decode", action="store_true", help="skip timing decode")
     p.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 forward")
     p.add_argument("--no-block", action="store_true", help="skip timing the attention layer")
-    p.add_argument("--no-b64", action="store_true", help="skip the step at batch 64")
+    p.add_argument("--no-b64", action="store_true",
+                   help="skip the step at batch 64 and at the other workload shapes")
     p.add_argument("--no-cold", action="store_true",
                    help="skip the steps after a cache-clearing scratch write")
     p.add_argument("--no-peaks", action="store_true",
@@ -387,7 +389,8 @@ def time_cold(step, stream, dev, n):
 
 
 def time_other_batch(w, stream, dev, K):
-    """The same step at another batch size (GPT-2 124M layer shape at B = 64)."""
+    """The same step on another workload: the GPT-2 124M layer at B = 64, and
+    the 16-head (350M) and T = 2048, 25-head shapes."""
     import numpy as np
     import torch
     from causal_flash_attention_amd import binding
@@ -824,6 +827,9 @@ def main(argv=None):
     hbm["frac"] = hbm["gbs"] / HBM_PEAK_GBS
     b64 = None if args.no_b64 else time_other_batch(BY_NAME["gpt2_124m_b64_t1024"], stream, dev,
                                                      min(K, 50))
+    others = None if args.no_b64 else {
+        n: time_other_batch(BY_NAME[n], stream, dev, min(K, 50))
+        for n in ("gpt2_350m_b16_t1024", "gpt2_1p5b_style_b4_t2048_h25")}
     peaks = None if args.no_peaks else measure_peaks(stream, dev)
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
@@ -878,6 +884,8 @@ def main(argv=None):
         result["pct_of_measured_bf16_peak"] = 100.0 * tflops / peaks["mfma_bf16_tflops"]
     if b64 is not None:
         result["b64"] = b64
+    if others is not None:
+        result["other_shapes"] = others
     if unfused is not None:
         unfused["fa_speedup"] = unfused["ms_per_step"] / ms_per_step
         result["unfused"] = unfused
