@@ -9,9 +9,8 @@
 // Any relabelling of k applied to both A and B leaves the product unchanged;
 // the kernels use that freedom to feed a C result back in as a B operand: the
 // 16 k of one MFMA step that lane half h supplies are then rows
-// {8*(j/4) + 4h + (j%4) : j = 0..7} of the C tile, and the operand that is
-// read from LDS is stored with its 16-element chunks permuted to match
-// (see perm16 below).
+// {8*(j/4) + 4h + (j%4) : j = 0..7} of the C tile, and the operand read
+// from LDS by transposing reads takes the same rows (atile_tr_offsets).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,11 +30,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int HEAD_DIM = 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-
-// Padded LDS row: 64 bf16 of data + 8 bf16 of padding (144 bytes), so that
-// 16 lanes reading 16 bytes each from 16 consecutive rows hit 64 distinct
-// banks.
-constexpr int LDS_ROW = 72;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -59,14 +53,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
-}
-
-__device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
-    *reinterpret_cast<u32x4*>(p) = v;
-}
-
 // Round 8 floats to nearest-even bf16 (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
                                             float a4, float a5, float a6, float a7) {
@@ -86,68 +72,6 @@ __device__ __forceinline__ u32x2 to_bf16x4_bits(float a0, float a1, float a2, fl
     f32x4 v = {a0, a1, a2, a3};
     bf16x4 b = __builtin_convertvector(v, bf16x4);
     return __builtin_bit_cast(u32x2, b);
-}
-
-// Position of element `k` (0..63) of a transposed LDS row: inside each group
-// of 16, the 4-element groups are stored in the order 0, 2, 1, 3, so that lane
-// half h reads its 8 operand elements {4h..4h+3, 8+4h..8+4h+3} as one
-// contiguous 16-byte chunk at offset 8h.
-__device__ __forceinline__ int perm16(int k) {
-    const int g = (k >> 2) & 3;
-    const int pg = ((g & 1) << 1) | (g >> 1);
-    return (k & ~15) | (pg << 2) | (k & 3);
-}
-
-// Staging of 64 x 64 bf16 tiles (rows [r0, r0 + 64) of a strided matrix)
-// through registers into LDS. Thread t (of 256) owns rows 2*(t%32) and
-// 2*(t%32)+1, column chunk t/32 (8 bf16). With this ownership the transposed
-// copy below is free of LDS bank conflicts: the 64 lanes of a wave write 64
-// distinct banks for every element.
-struct TilePair {
-    u32x4 a;  // row 2p
-    u32x4 b;  // row 2p + 1
-};
-
-__device__ __forceinline__ int tile_rp(int tid) { return tid & 31; }
-__device__ __forceinline__ int tile_cc(int tid) { return tid >> 5; }
-
-// Rows at or beyond `nrows` read as zero; `full` (uniform) promises that all
-// 64 rows exist and skips the checks.
-__device__ __forceinline__ TilePair load_tile_pair(const bf16* base, long long row_stride,
-                                                   int r0, int nrows, int tid, bool full) {
-    const int ra = r0 + 2 * tile_rp(tid), rb = ra + 1;
-    const bf16* pa = base + (long long)ra * row_stride + tile_cc(tid) * 8;
-    TilePair t;
-    if (full) {
-        t.a = *reinterpret_cast<const u32x4*>(pa);
-        t.b = *reinterpret_cast<const u32x4*>(pa + row_stride);
-    } else {
-        t.a = load16(pa, ra < nrows);
-        t.b = load16(pa + row_stride, rb < nrows);
-    }
-    return t;
-}
-
-// Row-major copy: lds[row][col], padded rows.
-__device__ __forceinline__ void store_tile_rows(bf16* lds, const TilePair& t, int tid) {
-    const int r = 2 * tile_rp(tid), c = tile_cc(tid) * 8;
-    lds_write16(lds + r * LDS_ROW + c, t.a);
-    lds_write16(lds + (r + 1) * LDS_ROW + c, t.b);
-}
-
-// Transposed copy: lds[col][perm16(row)], padded rows. Rows 2p and 2p+1 stay
-// adjacent under perm16, so each column pair is one 32-bit LDS write.
-__device__ __forceinline__ void store_tile_transposed(bf16* lds, const TilePair& t, int tid) {
-    const int pos = perm16(2 * tile_rp(tid));
-    bf16* col0 = lds + tile_cc(tid) * 8 * LDS_ROW + pos;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        // bytes {a.lo, b.lo} and {a.hi, b.hi} of word w: columns 2w and 2w+1
-        const unsigned int even = __builtin_amdgcn_perm(t.b[w], t.a[w], 0x05040100u);
-        const unsigned int odd = __builtin_amdgcn_perm(t.b[w], t.a[w], 0x07060302u);
-        *reinterpret_cast<unsigned int*>(col0 + (2 * w) * LDS_ROW) = even;
-        *reinterpret_cast<unsigned int*>(col0 + (2 * w + 1) * LDS_ROW) = odd;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -301,55 +225,6 @@ __device__ __forceinline__ bf16x8 atile_tr(lds_bf16* tile, int off0, int off1, i
     const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + kc * 16 * 64 + off1));
     const i16x4 v[2] = {a, b};
     return __builtin_bit_cast(bf16x8, v);
-}
-
-// The four A operands X^T of one d block (kc = 0..3) in one go: eight
-// transposing reads and a wait for them inside the same asm statement, so no
-// read is left in flight when the statement ends. (Through the compiler
-// intrinsic, each such read would make the compiler wait for every pending
-// direct global->LDS load first, which would drain the prefetch pipeline.)
-__device__ __forceinline__ void atile_tr4(lds_bf16* tile, int off0, int off1, bf16x8 out[4]) {
-    const unsigned int a0 = (unsigned int)(uintptr_t)(tile + off0);
-    const unsigned int a1 = (unsigned int)(uintptr_t)(tile + off1);
-    u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %7, %9 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-        : "v"(a0), "v"(a1));
-    const u32x2 lo[4] = {r0, r2, r4, r6}, hi[4] = {r1, r3, r5, r7};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        const u32x4 v = {lo[kc][0], lo[kc][1], hi[kc][0], hi[kc][1]};
-        out[kc] = as_bf16x8(v);
-    }
-}
-
-// Two consecutive chunks (KC0, KC0 + 1) of the operands read by atile_tr4.
-template <int KC0>
-__device__ __forceinline__ void atile_tr2(lds_bf16* tile, int off0, int off1, bf16x8 out[2]) {
-    const unsigned int a0 = (unsigned int)(uintptr_t)(tile + off0);
-    const unsigned int a1 = (unsigned int)(uintptr_t)(tile + off1);
-    u32x2 r0, r1, r2, r3;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(a1), "i"(KC0 * 2048), "i"((KC0 + 1) * 2048));
-    const u32x4 v0 = {r0[0], r0[1], r1[0], r1[1]};
-    const u32x4 v1 = {r2[0], r2[1], r3[0], r3[1]};
-    out[0] = as_bf16x8(v0);
-    out[1] = as_bf16x8(v1);
 }
 
 // Wait until at most n of this wave's vector-memory operations are pending.
