@@ -1,0 +1,44 @@
+"""Parity on seeded random shapes (needs a GPU): shapes the hand-picked edge
+lists do not name, drawn once from a fixed-seed generator, through the bf16,
+fp32 and FP8 paths against the same oracles and bars as the other parity
+tests (bf16: max-abs 1e-2 on O, 1e-3 on LSE, rel-L2 2e-2 on dQ, dK, dV;
+fp32: 1e-5 relative; FP8: the bounds of its forward test and rel-L2 2e-2 on
+its gradients against the FP8 oracle)."""
+
+import numpy as np
+import pytest
+
+from causal_flash_attention_amd import inputs as I
+
+from helpers import log
+from test_fp8_bwd_gpu import _check_grads, _inputs as fp8_inputs, _run_bwd
+from test_fp8_gpu import _check_forward
+from test_parity_gpu import _check_case
+
+pytestmark = pytest.mark.gpu
+
+D = 64
+_rng = np.random.default_rng(20261203)
+SHAPES = [(int(_rng.integers(1, 5)), int(_rng.integers(1, 701)), int(_rng.integers(1, 7)))
+          for _ in range(10)]
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES)
+def test_random_shape_bf16(B, T, H):
+    _check_case(B, T, H, "bf16", 1.0, 0.01, seed=5000 + T, label="random shape")
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES[:4])
+def test_random_shape_f32(B, T, H):
+    _check_case(B, T, H, "f32", 1.0, 1.0, seed=6000 + T, label="random shape")
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES[4:8])
+def test_random_shape_fp8(B, T, H):
+    log(f"[case] random shape fp8 B={B} T={T} H={H}")
+    qkv, dout = fp8_inputs(B, T, H, 1.0, 7000 + T)
+    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, 1.0)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    _check_forward(out64, lse64, I.to_float64(qkv, "bf16"), H, heads, f"random B={B} T={T} H={H}")
+    _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
+                 heads, f"random B={B} T={T} H={H}")
