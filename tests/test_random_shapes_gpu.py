@@ -42,3 +42,26 @@ def test_random_shape_fp8(B, T, H):
     _check_forward(out64, lse64, I.to_float64(qkv, "bf16"), H, heads, f"random B={B} T={T} H={H}")
     _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
                  heads, f"random B={B} T={T} H={H}")
+
+
+# A wide layer: 160 heads (C = 10240, a 60 KB packed row), where the tile
+# loads' 32-bit offsets span 64 rows of 30720 channels.
+WIDE = (1, 100, 160)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_layer(dtype):
+    B, T, H = WIDE
+    _check_case(B, T, H, dtype, 1.0, 0.01 if dtype == "bf16" else 1.0, seed=8100, label="wide",
+                heads=[(0, h) for h in (0, 1, 77, 158, 159)])
+
+
+def test_wide_layer_fp8():
+    B, T, H = WIDE
+    log(f"[case] wide layer fp8 B={B} T={T} H={H}")
+    qkv, dout = fp8_inputs(B, T, H, 1.0, 8200)
+    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, 1.0)
+    heads = [(0, h) for h in (0, 1, 77, 158, 159)]
+    _check_forward(out64, lse64, I.to_float64(qkv, "bf16"), H, heads, "wide")
+    _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
+                 heads, "wide")
