@@ -19,8 +19,11 @@
 //
 // The weight gradients are long contractions (K = B * T) with small outputs,
 // so they run split over K (as many splits as fill one round of workgroups)
-// into fp32 slabs that a second kernel adds in a fixed order; the bias gradients are column sums done the same way. No
-// atomics: the backward is deterministic.
+// into fp32 slabs that a second kernel adds in a fixed order; the bias
+// gradients are column sums done the same way. No atomics: the backward is
+// deterministic. The slab sum of each weight gradient shares a launch with
+// the column-sum partials of its bias, and the two bias sums end in one
+// launch.
 #include "attn_common.h"
 
 namespace cattn {
@@ -41,18 +44,18 @@ namespace {
 constexpr int COLSUM_ROWS = 256;  // rows per partial column sum
 constexpr int COLSUM_COLS = 512;  // columns per workgroup (64 threads x 8)
 
-// parts[s * N + n] = sum of X[r, n] over the COLSUM_ROWS rows r of chunk s.
-// Workgroup (column block, chunk s): thread t owns columns 8 (t % 64) .. +7
-// of the block (16-byte loads) and rows 64 (t / 64) .. +63 of the chunk,
-// summed in row order; the four row groups are then added in group order
-// through LDS. N must be a multiple of 8 and X's rows 16-byte aligned.
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const bf16* __restrict__ X,
-                                                             long long ld, int R, int N,
-                                                             float* __restrict__ parts) {
+// parts[s * N + n] = sum of X[r, n] over the COLSUM_ROWS rows r of chunk s,
+// for the column block `cb` and chunk `s` of one workgroup: thread t owns
+// columns 8 (t % 64) .. +7 of the block (16-byte loads) and rows
+// 64 (t / 64) .. +63 of the chunk, summed in row order; the four row groups
+// are then added in group order through LDS. N must be a multiple of 8 and
+// X's rows 16-byte aligned.
+__device__ __forceinline__ void colsum_partial(const bf16* __restrict__ X, long long ld, int R,
+                                               int N, float* __restrict__ parts, int cb, int s) {
     __shared__ float red[4][64][9];
     const int t = threadIdx.x, col8 = t & 63, grp = t >> 6;
-    const int n0 = blockIdx.x * COLSUM_COLS + 8 * col8;
-    const int r0 = blockIdx.y * COLSUM_ROWS + 64 * grp;
+    const int n0 = cb * COLSUM_COLS + 8 * col8;
+    const int r0 = s * COLSUM_ROWS + 64 * grp;
     const int r1 = min(R, r0 + 64);
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if (n0 < N) {
@@ -68,21 +71,21 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const bf16* __restr
     for (int e = 0; e < 8; ++e) red[grp][col8][e] = acc[e];
     __syncthreads();
     if (grp == 0 && n0 < N) {
-        float* out = parts + (long long)blockIdx.y * N + n0;
+        float* out = parts + (long long)s * N + n0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             out[e] = ((red[0][col8][e] + red[1][col8][e]) + red[2][col8][e]) + red[3][col8][e];
     }
 }
 
-// out[n] = sum over chunks of parts[s * N + n]: thread (column, group) sums
-// the chunks s = group, group + 4, ... in order, then the four groups are
-// added in group order.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ parts,
-                                                           int S, int N, float* __restrict__ out) {
+// out[n] = sum over chunks of parts[s * N + n] for the 64 columns of block
+// `cb`: thread (column, group) sums the chunks s = group, group + 4, ... in
+// order, then the four groups are added in group order.
+__device__ __forceinline__ void colsum_final(const float* __restrict__ parts, int S, int N,
+                                             float* __restrict__ out, int cb) {
     __shared__ float red[4][64];
     const int t = threadIdx.x, c = t & 63, grp = t >> 6;
-    const int n = blockIdx.x * 64 + c;
+    const int n = cb * 64 + c;
     float acc = 0.0f;
     if (n < N)
         for (int s = grp; s < S; s += 4) acc += parts[(long long)s * N + n];
@@ -91,26 +94,49 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
     if (grp == 0 && n < N) out[n] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
-// out[i] = sum over s = 0 .. S-1 of parts[s * n + i], in that order.
-__global__ __launch_bounds__(256) void sum_slabs_kernel(const float* __restrict__ parts, int S,
-                                                        long long n, float* __restrict__ out) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc += parts[(long long)s * n + i];
-    out[i] = acc;
+// One launch for two independent reductions that follow a weight-gradient
+// product: workgroups [0, nb_sum) add its K-split slabs (out[i] = sum over
+// s of slabs[s * n + i], in order, 256 elements per workgroup), the others
+// compute the column-sum partials of X (column block, then chunk).
+__global__ __launch_bounds__(256) void slabs_colsum_kernel(const float* __restrict__ slabs, int S,
+                                                           long long n, float* __restrict__ sum,
+                                                           int nb_sum, const bf16* __restrict__ X,
+                                                           long long ld, int R, int N,
+                                                           float* __restrict__ cparts, int n_cb) {
+    const int blk = blockIdx.x;
+    if (blk < nb_sum) {
+        const long long i = (long long)blk * 256 + threadIdx.x;
+        if (i >= n) return;
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) acc += slabs[(long long)s * n + i];
+        sum[i] = acc;
+        return;
+    }
+    const int c = blk - nb_sum;
+    colsum_partial(X, ld, R, N, cparts, c % n_cb, c / n_cb);
 }
 
-hipError_t colsum(const bf16* X, long long ld, int R, int N, float* parts, float* out,
-                  hipStream_t stream) {
-    const int chunks = (R + COLSUM_ROWS - 1) / COLSUM_ROWS;
-    hipLaunchKernelGGL(colsum_partial_kernel,
-                       dim3((unsigned)((N + COLSUM_COLS - 1) / COLSUM_COLS), (unsigned)chunks),
-                       dim3(256), 0, stream, X, ld, R, N, parts);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream,
-                       parts, chunks, N, out);
+// Both bias gradients from their column-sum partials: workgroups [0, nb1)
+// the first, the rest the second.
+__global__ __launch_bounds__(256) void colsum_final2_kernel(const float* __restrict__ p1, int N1,
+                                                            float* __restrict__ o1, int nb1,
+                                                            const float* __restrict__ p2, int N2,
+                                                            float* __restrict__ o2, int S) {
+    if ((int)blockIdx.x < nb1) colsum_final(p1, S, N1, o1, blockIdx.x);
+    else colsum_final(p2, S, N2, o2, blockIdx.x - nb1);
+}
+
+int colsum_chunks(int R) { return (R + COLSUM_ROWS - 1) / COLSUM_ROWS; }
+
+// The slab sum of a split product (when it has more than one slab) and the
+// column-sum partials of X, in one launch.
+hipError_t slabs_and_colsum(const float* slabs, int S, long long n, float* sum, const bf16* X,
+                            long long ld, int R, int N, float* cparts, hipStream_t stream) {
+    const int nb_sum = S > 1 ? (int)((n + 255) / 256) : 0;
+    const int n_cb = (N + COLSUM_COLS - 1) / COLSUM_COLS;
+    const long long blocks = nb_sum + (long long)n_cb * colsum_chunks(R);
+    hipLaunchKernelGGL(slabs_colsum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, slabs, S,
+                       n, sum, nb_sum, X, ld, R, N, cparts, n_cb);
     return hipGetLastError();
 }
 
@@ -135,18 +161,31 @@ int slabs_of(long long R, int splits) {
     return gemm_split_count((int)R, splits, &chunk);
 }
 
-long long block_workspace_floats(int B, int T, int H) {
+// Workspace (floats): the attention backward's delta, the K-split slabs of
+// the larger weight gradient, then the column-sum partials of dy (chunks x C)
+// and of dqkv (chunks x 3C).
+struct BlockWs {
+    long long delta, slabs, cp_proj, cp_attn, total;
+};
+
+BlockWs block_ws(int B, int T, int H) {
     const long long C = (long long)H * HEAD_DIM, R = (long long)B * T;
     const long long tp = ((long long)T + 63) / 64 * 64;
-    const long long delta = 10LL * B * H * tp;
     const long long s_attn = slabs_of(R, block_splits(R, (int)C, (int)(3 * C)));
     const long long s_proj = slabs_of(R, block_splits(R, (int)C, (int)C));
-    long long parts = s_attn * C * 3 * C;
-    if (s_proj * C * C > parts) parts = s_proj * C * C;
-    const long long cs = (R + COLSUM_ROWS - 1) / COLSUM_ROWS * 3 * C;
-    if (cs > parts) parts = cs;
-    return delta + parts;
+    long long slabs = s_attn * C * 3 * C;
+    if (s_proj * C * C > slabs) slabs = s_proj * C * C;
+    const long long chunks = colsum_chunks((int)R);
+    BlockWs w;
+    w.delta = 0;
+    w.slabs = 10LL * B * H * tp;
+    w.cp_proj = w.slabs + slabs;
+    w.cp_attn = w.cp_proj + chunks * C;
+    w.total = w.cp_attn + chunks * 3 * C;
+    return w;
 }
+
+long long block_workspace_floats(int B, int T, int H) { return block_ws(B, T, H).total; }
 
 hipError_t launch_attn_block_fwd_bf16(const void* x, const void* w_attn, const void* b_attn,
                                       const void* w_proj, const void* b_proj, void* qkv, void* att,
@@ -170,9 +209,11 @@ hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void*
                                       hipStream_t stream) {
     const long long C = (long long)H * HEAD_DIM;
     const int R = B * T;
-    const long long tp = ((long long)T + 63) / 64 * 64;
-    float* delta = ws;
-    float* parts = ws + 10LL * B * H * tp;
+    const BlockWs w = block_ws(B, T, H);
+    float* delta = ws + w.delta;
+    float* parts = ws + w.slabs;
+    float* cp_proj = ws + w.cp_proj;
+    float* cp_attn = ws + w.cp_attn;
     // c_proj backward
     hipError_t e = launch_gemm_bf16(false, false, false, dy, C, w_proj, C, datt, C, nullptr, R,
                                     (int)C, (int)C, 1, stream);
@@ -181,13 +222,9 @@ hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void*
     if ((e = launch_gemm_bf16(true, true, true, att, C, dy, C, sp > 1 ? parts : dw_proj, C,
                               nullptr, (int)C, (int)C, R, sp_ask, stream)) != hipSuccess)
         return e;
-    if (sp > 1) {
-        hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((C * C + 255) / 256)), dim3(256), 0,
-                           stream, parts, sp, C * C, dw_proj);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if ((e = colsum(static_cast<const bf16*>(dy), C, R, (int)C, parts, db_proj, stream)) !=
-        hipSuccess)
+    // dW_proj's slab sum and db_proj's column-sum partials
+    if ((e = slabs_and_colsum(parts, sp, C * C, dw_proj, static_cast<const bf16*>(dy), C, R,
+                              (int)C, cp_proj, stream)) != hipSuccess)
         return e;
     // attention backward: dqkv from datt (the dO of the attention)
     if ((e = launch_attn_bwd_dq_pre_bf16(qkv, datt, att, lse, delta, dqkv, B, T, H, stream)) !=
@@ -204,12 +241,15 @@ hipError_t launch_attn_block_bwd_bf16(const void* dy, const void* x, const void*
                               3 * C, nullptr, (int)C, (int)(3 * C), R, sa_ask, stream)) !=
         hipSuccess)
         return e;
-    if (sa > 1) {
-        hipLaunchKernelGGL(sum_slabs_kernel, dim3((unsigned)((C * 3 * C + 255) / 256)), dim3(256),
-                           0, stream, parts, sa, C * 3 * C, dw_attn);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return colsum(static_cast<const bf16*>(dqkv), 3 * C, R, (int)(3 * C), parts, db_attn, stream);
+    // dW_attn's slab sum and db_attn's column-sum partials, then both bias sums
+    if ((e = slabs_and_colsum(parts, sa, C * 3 * C, dw_attn, static_cast<const bf16*>(dqkv),
+                              3 * C, R, (int)(3 * C), cp_attn, stream)) != hipSuccess)
+        return e;
+    const int nb1 = (int)((C + 63) / 64), nb2 = (int)((3 * C + 63) / 64);
+    hipLaunchKernelGGL(colsum_final2_kernel, dim3((unsigned)(nb1 + nb2)), dim3(256), 0, stream,
+                       cp_proj, (int)C, db_proj, nb1, cp_attn, (int)(3 * C), db_attn,
+                       colsum_chunks(R));
+    return hipGetLastError();
 }
 
 }  // namespace cattn
