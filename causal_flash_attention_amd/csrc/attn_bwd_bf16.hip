@@ -313,17 +313,22 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     const bf16x8 bd = hf == 0 ? zero8 : neg3;
     // Issue the loads of query tile `it` (relative) into stage `st`: Q and dO
     // by every wave, the tile's 2 KB of terms by waves 0 and 1 (1 KB each).
-    auto issue = [&](int it, int st) {
+    // Wave-uniform LDS byte addresses of stage 0 (stage st sits st stages on).
+    const unsigned int q_lds = atile_addr(sm.q[0]), g_lds = atile_addr(sm.g[0]);
+    const unsigned int t_lds = atile_addr(sm.terms[0]);
+    constexpr unsigned int STAGE_BYTES = ATILE_ELEMS * 2, TSTAGE_BYTES = KV_BM * 16 * 2;
+    auto issue = [&](int it) {
+        const unsigned int st = (unsigned int)it % NSTAGE;
         const int q0 = (qt_begin + it) * KV_BM;
-        atile_load(atile_addr(sm.q[st]), rows_rsrc(qbase, rs, q0, T), 0, ld_rs);
-        atile_load(atile_addr(sm.g[st]), rows_rsrc(gbase, C, q0, T), 0, ld_C);
+        atile_load(q_lds + st * STAGE_BYTES, rows_rsrc(qbase, rs, q0, T), 0, ld_rs);
+        atile_load(g_lds + st * STAGE_BYTES, rows_rsrc(gbase, C, q0, T), 0, ld_C);
         if (wave < 2)
             lds_dma16(terms_rows + (long long)(q0 + 32 * wave) * 32 + lane * 16,
-                      atile_addr(sm.terms[st] + wave * 512));
+                      __builtin_amdgcn_readfirstlane(t_lds + st * TSTAGE_BYTES + wave * 1024));
     };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < n_it) issue(j, j);
+        if (j < n_it) issue(j);
 
     // K and V of this lane's key as B operands (of S = Q K^T and dP = dO V^T).
     bf16x8 kreg[4], vreg[4];
@@ -354,12 +359,12 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
             wait_vmem<0>();
         }
         __syncthreads();
-        if (it + NSTAGE - 1 < n_it) issue(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+        if (it + NSTAGE - 1 < n_it) issue(it + NSTAGE - 1);
         const int q0 = (qt_begin + it) * KV_BM;
-        const int st = it % NSTAGE;
-        lds_bf16* qt = atile_view(sm.q[st]);
-        lds_bf16* gt = atile_view(sm.g[st]);
-        lds_bf16* terms = atile_view(sm.terms[st]);
+        const unsigned int st = (unsigned int)it % NSTAGE;
+        lds_bf16* qt = atile_view_at(q_lds + st * STAGE_BYTES);
+        lds_bf16* gt = atile_view_at(g_lds + st * STAGE_BYTES);
+        lds_bf16* terms = atile_view_at(t_lds + st * TSTAGE_BYTES);
         const int lim = my_k - q0 - 4 * hf;
         if (decltype(maybe_diag)::value) {
             if (q0 + KV_BM - 1 < kw) return;  // every query of the tile precedes this wave's keys
@@ -505,14 +510,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
 
     // K and V rows [k0, k0 + 64) into stage st: one descriptor, since V sits
     // C elements after K in every packed row.
-    auto issue = [&](int k0, int st) {
-        const i32x4 kv = rows_rsrc(kbase, rs, k0, T);
-        atile_load(atile_addr(sm.k[st]), kv, 0, ld_rs);
-        atile_load(atile_addr(sm.v[st]), kv, 2u * C, ld_rs);
+    const unsigned int k_lds = atile_addr(sm.k[0]), v_lds = atile_addr(sm.v[0]);
+    constexpr unsigned int STAGE_BYTES = ATILE_ELEMS * 2;
+    auto issue = [&](int t) {
+        const unsigned int st = (unsigned int)t % NSTAGE;
+        const i32x4 kv = rows_rsrc(kbase, rs, t * DQ_BN, T);
+        atile_load(k_lds + st * STAGE_BYTES, kv, 0, ld_rs);
+        atile_load(v_lds + st * STAGE_BYTES, kv, 2u * C, ld_rs);
     };
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < n_kt) issue(j * DQ_BN, j);
+        if (j < n_kt) issue(j);
 
     bf16x8 qreg[4], greg[4];
     {
@@ -545,12 +553,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
         if (j + 1 < n_kt) wait_vmem<4>();
         else wait_vmem<0>();
         __syncthreads();
-        if (j + NSTAGE - 1 < n_kt) issue((j + NSTAGE - 1) * DQ_BN, (j + NSTAGE - 1) % NSTAGE);
+        if (j + NSTAGE - 1 < n_kt) issue(j + NSTAGE - 1);
         const int k0 = j * DQ_BN;
         if (k0 > qw + 31) continue;  // whole tile after this wave's queries
-        const int st = j % NSTAGE;
-        lds_bf16* kt = atile_view(sm.k[st]);
-        lds_bf16* vt = atile_view(sm.v[st]);
+        const unsigned int st = (unsigned int)j % NSTAGE;
+        lds_bf16* kt = atile_view_at(k_lds + st * STAGE_BYTES);
+        lds_bf16* vt = atile_view_at(v_lds + st * STAGE_BYTES);
         const int lim = my_q - k0 - 4 * hf;
         if (k0 == (qw & ~(DQ_BN - 1)))  // the tile holding this wave's diagonal
             dq_tile<true>(kt, vt, qreg, greg, roff, troff, dqt, lim, lse2, dd, c_log2);

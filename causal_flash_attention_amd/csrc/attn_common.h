@@ -193,6 +193,12 @@ __device__ __forceinline__ lds_bf16* atile_view(const bf16* tile) {
     return (lds_bf16*)(uintptr_t)a;
 }
 
+// The same for a tile given by its LDS byte address.
+__device__ __forceinline__ lds_bf16* atile_view_at(unsigned int a) {
+    asm volatile("" : "+v"(a));
+    return (lds_bf16*)(uintptr_t)a;
+}
+
 // Row-major operand: 8 bf16 of tile row r, logical 16-byte chunk c.
 __device__ __forceinline__ bf16x8 atile_row(lds_bf16* tile, int r, int c) {
     typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;

@@ -220,15 +220,19 @@ __global__ __launch_bounds__(256, CATTN_FP8_WAVES_PER_SIMD) void attn_fwd_fp8_ke
     const unsigned int voff_v = (unsigned int)(lrow * Tp + 16 * (lpos ^ swz_v(lrow)));
     const unsigned int voff_e = (unsigned int)(16 * lane);
     const unsigned int wave_lds = __builtin_amdgcn_readfirstlane((unsigned int)(1024 * wave));
-    auto issue = [&](int j, int st) {
-        lds_dma16_buf(rs_k, voff_k, (unsigned int)(j * 64 * 64), lds_addr_u(sm.k[st]) + wave_lds);
-        lds_dma16_buf(rs_v, voff_v, (unsigned int)(j * 64), lds_addr_u(sm.v[st]) + wave_lds);
+    // Wave-uniform LDS byte addresses of stage 0; stage st sits st stages on.
+    const unsigned int k_l = lds_addr_u(sm.k[0]), v_l = lds_addr_u(sm.v[0]), e_l = lds_addr_u(sm.e[0]);
+    constexpr unsigned int K_ST = sizeof(sm.k[0]), V_ST = sizeof(sm.v[0]), E_ST = sizeof(sm.e[0]);
+    auto issue = [&](int j) {
+        const unsigned int st = (unsigned int)j % NSTAGE;
+        lds_dma16_buf(rs_k, voff_k, (unsigned int)(j * 64 * 64), k_l + st * K_ST + wave_lds);
+        lds_dma16_buf(rs_v, voff_v, (unsigned int)(j * 64), v_l + st * V_ST + wave_lds);
         if (wave == 0 && lane < 16)
-            lds_dma16_buf(rs_e, voff_e, (unsigned int)(j * F8_EXP_TILE + 128), lds_addr_u(sm.e[st]));
+            lds_dma16_buf(rs_e, voff_e, (unsigned int)(j * F8_EXP_TILE + 128), e_l + st * E_ST);
     };
 #pragma unroll
     for (int j = 0; j < PREFETCH; ++j)
-        if (j < n_kt) issue(j, j);
+        if (j < n_kt) issue(j);
 
     // Q^T operand (B of S^T): channels [16h, 16h + 16) and [32 + 16h, +16) of
     // this lane's query, with the exponent of channel block h.
@@ -267,11 +271,12 @@ __global__ __launch_bounds__(256, CATTN_FP8_WAVES_PER_SIMD) void attn_fwd_fp8_ke
             wait_vmem<0>();
         }
         __syncthreads();
-        if (j + PREFETCH < n_kt) issue(j + PREFETCH, (j + PREFETCH) % NSTAGE);
+        if (j + PREFETCH < n_kt) issue(j + PREFETCH);
         if (j > j_last) continue;  // tiles above this wave's diagonal
-        lds_u8* kt = lds_view(sm.k[j % NSTAGE]);
-        lds_u8* vt = lds_view(sm.v[j % NSTAGE]);
-        lds_u8* et = lds_view(sm.e[j % NSTAGE]);
+        const unsigned int st = (unsigned int)j % NSTAGE;
+        lds_u8* kt = lds_view_at(k_l + st * K_ST);
+        lds_u8* vt = lds_view_at(v_l + st * V_ST);
+        lds_u8* et = lds_view_at(e_l + st * E_ST);
         f32x16 s[2];
         scores_f8(kt, et, o, qop, qs, s);
         const i32x8 va = lds_operand(vt, o.v[0]);

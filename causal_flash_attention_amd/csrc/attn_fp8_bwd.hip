@@ -288,19 +288,24 @@ __global__ __launch_bounds__(256, CATTN_FP8_DQ_WAVES_PER_SIMD) void attn_bwd_fp8
     const unsigned int voff_r = (unsigned int)(lrow * 64 + 16 * (lpos ^ swz_k(lrow)));
     const unsigned int voff_c = (unsigned int)(lrow * Tp + 16 * (lpos ^ swz_v(lrow)));
     const unsigned int wave_lds = __builtin_amdgcn_readfirstlane((unsigned int)(1024 * wave));
-    auto issue = [&](int j, int st) {
-        lds_dma16_buf(rs_k, voff_r, (unsigned int)(j * 4096), lds_addr_u(sm.k[st]) + wave_lds);
-        lds_dma16_buf(rs_v, voff_r, (unsigned int)(j * 4096), lds_addr_u(sm.v[st]) + wave_lds);
-        lds_dma16_buf(rs_kt, voff_c, (unsigned int)(j * 64), lds_addr_u(sm.kt[st]) + wave_lds);
+    // Wave-uniform LDS byte addresses of stage 0; stage st sits st stages on.
+    const unsigned int k_l = lds_addr_u(sm.k[0]), v_l = lds_addr_u(sm.v[0]);
+    const unsigned int c_l = lds_addr_u(sm.kt[0]), e_l = lds_addr_u(sm.e[0]);
+    constexpr unsigned int K_ST = sizeof(sm.k[0]), C_ST = sizeof(sm.kt[0]), E_ST = sizeof(sm.e[0]);
+    auto issue = [&](int j) {
+        const unsigned int st = (unsigned int)j % NSTAGE;
+        lds_dma16_buf(rs_k, voff_r, (unsigned int)(j * 4096), k_l + st * K_ST + wave_lds);
+        lds_dma16_buf(rs_v, voff_r, (unsigned int)(j * 4096), v_l + st * K_ST + wave_lds);
+        lds_dma16_buf(rs_kt, voff_c, (unsigned int)(j * 64), c_l + st * C_ST + wave_lds);
         if (wave == 0 && lane < 8)   // K exponents of the forward buffer
             lds_dma16_buf(rs_fe, (unsigned int)(128 + 16 * lane), (unsigned int)(j * 384),
-                          lds_addr_u(sm.e[st]));
+                          e_l + st * E_ST);
         if (wave == 1 && lane < 16)  // V and K position-block exponents
             lds_dma16_buf(rs_sd, (unsigned int)(16 * lane), (unsigned int)(j * SIDE_TILE),
-                          lds_addr_u(sm.e[st]) + 128);
+                          e_l + st * E_ST + 128);
     };
-    issue(0, 0);
-    if (n_kt > 1) issue(1, 1);
+    issue(0);
+    if (n_kt > 1) issue(1);
 
     // B operands of the lane's query: Q and dO in channel blocks.
     const int q = qw + l32;
@@ -332,13 +337,13 @@ __global__ __launch_bounds__(256, CATTN_FP8_DQ_WAVES_PER_SIMD) void attn_bwd_fp8
             wait_vmem<0>();
         }
         __syncthreads();
-        if (j + 2 < n_kt) issue(j + 2, (j + 2) % NSTAGE);
+        if (j + 2 < n_kt) issue(j + 2);
         if (j > j_last) continue;
-        const int st = j % NSTAGE;
-        lds_u8* kt = lds_view(sm.k[st]);
-        lds_u8* vt = lds_view(sm.v[st]);
-        lds_u8* ct = lds_view(sm.kt[st]);
-        lds_u8* et = lds_view(sm.e[st]);
+        const unsigned int st = (unsigned int)j % NSTAGE;
+        lds_u8* kt = lds_view_at(k_l + st * K_ST);
+        lds_u8* vt = lds_view_at(v_l + st * K_ST);
+        lds_u8* ct = lds_view_at(c_l + st * C_ST);
+        lds_u8* et = lds_view_at(e_l + st * E_ST);
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -428,17 +433,23 @@ __global__ __launch_bounds__(256, CATTN_FP8_DKDV_WAVES_PER_SIMD) void attn_bwd_f
     const unsigned int voff_r = (unsigned int)(lrow * 64 + 16 * (lpos ^ swz_k(lrow)));
     const unsigned int voff_c = (unsigned int)(lrow * Tp + 16 * (lpos ^ swz_v(lrow)));
     const unsigned int wave_lds = __builtin_amdgcn_readfirstlane((unsigned int)(1024 * wave));
-    auto issue = [&](int j, int st) {
-        lds_dma16_buf(rs_q, voff_r, (unsigned int)(j * 4096), lds_addr_u(sm.q[st]) + wave_lds);
-        lds_dma16_buf(rs_g, voff_r, (unsigned int)(j * 4096), lds_addr_u(sm.g[st]) + wave_lds);
-        lds_dma16_buf(rs_qt, voff_c, (unsigned int)(j * 64), lds_addr_u(sm.qt[st]) + wave_lds);
-        lds_dma16_buf(rs_gt, voff_c, (unsigned int)(j * 64), lds_addr_u(sm.gt[st]) + wave_lds);
+    // Wave-uniform LDS byte addresses of stage 0; stage st sits st stages on.
+    const unsigned int q_l = lds_addr_u(sm.q[0]), g_l = lds_addr_u(sm.g[0]);
+    const unsigned int qc_l = lds_addr_u(sm.qt[0]), gc_l = lds_addr_u(sm.gt[0]);
+    const unsigned int e_l = lds_addr_u(sm.e[0]);
+    constexpr unsigned int R_ST = sizeof(sm.q[0]), C_ST = sizeof(sm.qt[0]), E_ST = sizeof(sm.e[0]);
+    auto issue = [&](int j, int it) {
+        const unsigned int st = (unsigned int)it % NSTAGE;
+        lds_dma16_buf(rs_q, voff_r, (unsigned int)(j * 4096), q_l + st * R_ST + wave_lds);
+        lds_dma16_buf(rs_g, voff_r, (unsigned int)(j * 4096), g_l + st * R_ST + wave_lds);
+        lds_dma16_buf(rs_qt, voff_c, (unsigned int)(j * 64), qc_l + st * C_ST + wave_lds);
+        lds_dma16_buf(rs_gt, voff_c, (unsigned int)(j * 64), gc_l + st * C_ST + wave_lds);
         if (wave == 0 && lane < 56)  // dO, Q, dO exponents, LSE2, D of the side tile
             lds_dma16_buf(rs_sd, (unsigned int)(SD_G + 16 * lane), (unsigned int)(j * SIDE_TILE),
-                          lds_addr_u(sm.e[st]) + 128);
+                          e_l + st * E_ST + 128);
         if (wave == 1 && lane < 8)   // Q exponents of the forward buffer
             lds_dma16_buf(rs_fe, (unsigned int)(16 * lane), (unsigned int)(j * 384),
-                          lds_addr_u(sm.e[st]));
+                          e_l + st * E_ST);
     };
     issue(j0, 0);
     if (n_steps > 1) issue(j0 + 1, 1);
@@ -470,14 +481,14 @@ __global__ __launch_bounds__(256, CATTN_FP8_DKDV_WAVES_PER_SIMD) void attn_bwd_f
             wait_vmem<0>();
         }
         __syncthreads();
-        if (it + 2 < n_steps) issue(j + 2, (it + 2) % NSTAGE);
+        if (it + 2 < n_steps) issue(j + 2, it + 2);
         if (64 * j + 63 < kw) continue;  // every query of the tile is before the wave's keys
-        const int st = it % NSTAGE;
-        lds_u8* qt_ = lds_view(sm.q[st]);
-        lds_u8* gt_ = lds_view(sm.g[st]);
-        lds_u8* qpt = lds_view(sm.qt[st]);
-        lds_u8* gpt = lds_view(sm.gt[st]);
-        lds_u8* et = lds_view(sm.e[st]);
+        const unsigned int st = (unsigned int)it % NSTAGE;
+        lds_u8* qt_ = lds_view_at(q_l + st * R_ST);
+        lds_u8* gt_ = lds_view_at(g_l + st * R_ST);
+        lds_u8* qpt = lds_view_at(qc_l + st * C_ST);
+        lds_u8* gpt = lds_view_at(gc_l + st * C_ST);
+        lds_u8* et = lds_view_at(e_l + st * E_ST);
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {

@@ -101,6 +101,12 @@ __device__ __forceinline__ lds_u8* lds_view(const u8* p) {
     return (lds_u8*)(uintptr_t)a;
 }
 
+// The same for a tile given by its LDS byte address.
+__device__ __forceinline__ lds_u8* lds_view_at(unsigned int a) {
+    asm volatile("" : "+v"(a));
+    return (lds_u8*)(uintptr_t)a;
+}
+
 __device__ __forceinline__ unsigned int lds_addr_u(const u8* p) {
     return __builtin_amdgcn_readfirstlane((unsigned int)(uintptr_t)(lds_u8*)p);
 }

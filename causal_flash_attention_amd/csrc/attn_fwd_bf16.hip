@@ -185,15 +185,29 @@ __global__ __launch_bounds__(256, CATTN_FWD_WAVES_PER_SIMD) void attn_fwd_bf16_k
 #pragma unroll
     for (int db = 0; db < 2; ++db) atile_tr_offsets(lane, db, &voff[db][0], &voff[db][1]);
 
-    // K and V rows [k0, k0 + 64) into stage st: one descriptor, since V sits
-    // C elements after K in every packed row.
-    auto issue = [&](int k0, int st) {
-        const i32x4 kv = rows_rsrc(kbase, rs, k0, T);
-        atile_load(atile_addr(sm.k[st]), kv, 0, ld_rs);
-        atile_load(atile_addr(sm.v[st]), kv, 2u * C, ld_rs);
+    // Wave-uniform LDS byte addresses of stage 0 (stage st sits st * 8 KB on).
+    const unsigned int k_lds = atile_addr(sm.k[0]), v_lds = atile_addr(sm.v[0]);
+    constexpr unsigned int STAGE_BYTES = ATILE_ELEMS * 2;
+    // K and V rows of tile t into stage t % 3: one descriptor, since V sits C
+    // elements after K in every packed row. 32-bit LDS addresses and a
+    // descriptor derived from t keep the per-tile scalar work small.
+    const long long tile_bytes = (long long)FWD_BN * rs * 2;
+    const unsigned long long k_at = (unsigned long long)(uintptr_t)kbase;
+    const long long k_total = (long long)T * rs * 2;
+    auto issue = [&](int t) {
+        const unsigned int st = (unsigned int)t % NSTAGE;
+        const unsigned long long at = k_at + (unsigned long long)t * tile_bytes;
+        const long long left = k_total - (long long)t * tile_bytes;
+        i32x4 kv;
+        kv.x = (int)(unsigned int)at;
+        kv.y = (int)((unsigned int)(at >> 32) & 0xffffu);
+        kv.z = (int)(left > 0xffffffffLL ? 0xffffffffu : (unsigned int)left);
+        kv.w = 0x00020000;
+        atile_load(k_lds + st * STAGE_BYTES, kv, 0, ld_rs);
+        atile_load(v_lds + st * STAGE_BYTES, kv, 2u * C, ld_rs);
     };
-    issue(0, 0);
-    if (n_kt > 1) issue(FWD_BN, 1);
+    issue(0);
+    if (n_kt > 1) issue(1);
 
     // Q^T operands (B of S^T = K Q^T): d = 16kk + 8hf .. +7 of this lane's query.
     bf16x8 qreg[4];
@@ -212,20 +226,21 @@ __global__ __launch_bounds__(256, CATTN_FWD_WAVES_PER_SIMD) void attn_fwd_bf16_k
     f32x16 acc[2] = {zero16(), zero16()};  // O^T per d block
     f32x16 s[2], s_next[2];
     {
-        scores(atile_view(sm.k[0]), koff, qreg, s);
+        scores(atile_view_at(k_lds), koff, qreg, s);
         if (j_last == 0) mask_tile(s, qw + l32 - 4 * hf);
         update_max(tile_max(s, c_log2), m_run, l_run, acc);
     }
 
     auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        const unsigned int sj = (unsigned int)j % NSTAGE, sn = (unsigned int)(j + 1) % NSTAGE;
         // Tile j+1 (issued one step ago) has landed everywhere, and every wave
         // has left step j-1, so its stage can take tile j+2.
         wait_vmem<0>();
         __syncthreads();
-        if (j + 2 < n_kt) issue((j + 2) * FWD_BN, (j + 2) % NSTAGE);
+        if (j + 2 < n_kt) issue(j + 2);
         if (j > j_last) return;  // tiles above this wave's diagonal
-        lds_bf16* vt = atile_view(sm.v[j % NSTAGE]);
-        lds_bf16* kt_next = atile_view(sm.k[(j + 1) % NSTAGE]);
+        lds_bf16* vt = atile_view_at(v_lds + sj * STAGE_BYTES);
+        lds_bf16* kt_next = atile_view_at(k_lds + sn * STAGE_BYTES);
         const int lim_next = qw - (j + 1) * FWD_BN + l32 - 4 * hf;
         if (j + 1 < j_last)
             tile_step<NEXT_PLAIN>(cur, nxt, kt_next, vt, koff, voff, qreg, acc, m_run, l_run,
