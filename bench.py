@@ -110,6 +110,10 @@ def parse_args(argv=None):
                    help="rocprofv3 --pmc output with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, "
                         "SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE")
     p.add_argument("--mfma-command", default="", help="the command that produced --mfma-dir")
+    p.add_argument("--wave-dirs", nargs="*", default=[],
+                   help="rocprofv3 --pmc outputs that together hold the SQ_WAVE_CYCLES, "
+                        "SQ_ACTIVE_INST_*, SQ_WAIT_*, SQ_WAVES and SQ_INSTS_* counters")
+    p.add_argument("--wave-command", default="", help="the commands that produced --wave-dirs")
     p.add_argument("--profile-command", default="",
                    help="the commands that produced the CSVs, recorded in the summaries")
     return p.parse_args(argv)
@@ -236,6 +240,57 @@ def write_mfma_profile(args, w) -> None:
     print(path)
 
 
+WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                 "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                 "SQ_ACTIVE_INST_MISC", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAVES",
+                 "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS")
+
+
+def write_wave_profile(args, w) -> None:
+    """Where the waves of each kernel spend their cycles, from two counter
+    passes: the share of wave-cycles spent issuing (by instruction type),
+    waiting on a dependency (s_waitcnt, barrier) and ready but not issued
+    (another wave held the unit), and the instructions issued per wave."""
+    per = {}  # kernel -> counter -> per-dispatch totals
+    for d in args.wave_dirs:
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = _kernel_of(r["Kernel_Name"])
+            if k is None or r["Counter_Name"] not in WAVE_COUNTERS:
+                continue
+            key = (k, r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (k, _, c), v in acc.items():
+            per.setdefault(k, {}).setdefault(c, []).append(v)
+    lines = [f"# Wave cycles per kernel, workload {w.name}, from rocprofv3 counters",
+             f"# command: {args.wave_command or '(see the bench.py --write-profiles invocation)'}",
+             "# shares of SQ_WAVE_CYCLES (medians over the dispatches): issuing = SQ_ACTIVE_INST_ANY "
+             "(valu, salu, lds, vmem, misc: SQ_ACTIVE_INST_*), waiting = SQ_WAIT_ANY (s_waitcnt, "
+             "barrier), not_issued = SQ_WAIT_INST_ANY (ready, another wave held the unit);",
+             "# per_wave = SQ_INSTS_* / SQ_WAVES",
+             "# kernel, dispatches, issuing, valu, salu, lds, vmem, misc, waiting, not_issued, "
+             "valu_per_wave, mfma_per_wave, salu_per_wave, lds_per_wave"]
+    order = list(KERNELS) + [k for k in sorted(per) if k not in KERNELS]
+    for k in order:
+        d = per.get(k)
+        if not d or any(c not in d for c in WAVE_COUNTERS):
+            continue
+        m = {c: statistics.median(v) for c, v in d.items()}
+        wc, nw = m["SQ_WAVE_CYCLES"], m["SQ_WAVES"]
+        share = [m[c] / wc for c in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                                     "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS",
+                                     "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_MISC", "SQ_WAIT_ANY",
+                                     "SQ_WAIT_INST_ANY")]
+        insts = [m[c] / nw for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+                                     "SQ_INSTS_LDS")]
+        lines.append(f"{k}, {len(d['SQ_WAVES'])}, " + ", ".join(f"{x:.3f}" for x in share) + ", " +
+                     ", ".join(f"{x:.0f}" for x in insts))
+    path = os.path.join(PROFILE_DIR, f"wave_cycles_{w.name}.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def write_profiles(args, w) -> int:
     """Turn rocprofv3 CSV output into the text summaries under profiles/."""
     os.makedirs(PROFILE_DIR, exist_ok=True)
@@ -272,6 +327,8 @@ def write_profiles(args, w) -> int:
         print(path)
     if args.mfma_dir:
         write_mfma_profile(args, w)
+    if args.wave_dirs:
+        write_wave_profile(args, w)
     if args.fetch_dir and args.write_dir:
         fetch = _counter_means(args.fetch_dir, "FETCH_SIZE")
         write = _counter_means(args.write_dir, "WRITE_SIZE")
