@@ -258,14 +258,18 @@ __global__ __launch_bounds__(64 * ROWS_PER_WG) void softmax_rows_kernel(
     if (lane == 0) lse[row] = m + logf(sum);
 }
 
-// D = sum_j P dP and dS = P (dP - D), bf16 (0 in the padding, where P = 0).
+// D = sum_j P dP and dS = P (dP - D), bf16, over the visible keys j <= i of
+// row i; dS is 0 above the diagonal and in the padding. dP holds only the T
+// columns its product wrote: the padding columns are never read, since 0 times
+// whatever they hold (possibly not a number) must not reach D.
 template <int VPT>
 __global__ __launch_bounds__(64 * ROWS_PER_WG) void softmax_bwd_rows_kernel(
-    const bf16* __restrict__ P, const float* __restrict__ dP, bf16* __restrict__ dS, int Tp8,
-    long long n_rows) {
+    const bf16* __restrict__ P, const float* __restrict__ dP, bf16* __restrict__ dS, int T,
+    int Tp8, long long n_rows) {
     const long long row = (long long)blockIdx.x * ROWS_PER_WG + (threadIdx.x >> 6);
     if (row >= n_rows) return;
     const int lane = threadIdx.x & 63;
+    const int i = (int)(row % T);
     const bf16* p = P + row * Tp8;
     const float* g = dP + row * Tp8;
     float pv[VPT], gv[VPT];
@@ -281,8 +285,9 @@ __global__ __launch_bounds__(64 * ROWS_PER_WG) void softmax_bwd_rows_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            pv[4 * c + e] = (float)pp[e];
-            gv[4 * c + e] = gg[e];
+            const bool vis = j0 + e <= i;
+            pv[4 * c + e] = vis ? (float)pp[e] : 0.0f;
+            gv[4 * c + e] = vis ? gg[e] : 0.0f;
             acc = fmaf(pv[4 * c + e], gv[4 * c + e], acc);
         }
     }
@@ -290,10 +295,12 @@ __global__ __launch_bounds__(64 * ROWS_PER_WG) void softmax_bwd_rows_kernel(
 #pragma unroll
     for (int c = 0; c < VPT / 4; ++c) {
         const int j0 = 4 * lane + 256 * c;
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            d[e] = j0 + e <= i ? pv[4 * c + e] * (gv[4 * c + e] - D) : 0.0f;
         if (j0 < Tp8)
-            *reinterpret_cast<u32x2*>(dS + row * Tp8 + j0) = to_bf16x4_bits(
-                pv[4 * c] * (gv[4 * c] - D), pv[4 * c + 1] * (gv[4 * c + 1] - D),
-                pv[4 * c + 2] * (gv[4 * c + 2] - D), pv[4 * c + 3] * (gv[4 * c + 3] - D));
+            *reinterpret_cast<u32x2*>(dS + row * Tp8 + j0) = to_bf16x4_bits(d[0], d[1], d[2], d[3]);
     }
 }
 
@@ -307,12 +314,12 @@ hipError_t launch_softmax(const float* S, bf16* P, float* lse, int T, int Tp8, l
     return hipGetLastError();
 }
 
-hipError_t launch_softmax_bwd(const bf16* P, const float* dP, bf16* dS, int Tp8, long long n_rows,
-                              hipStream_t stream) {
+hipError_t launch_softmax_bwd(const bf16* P, const float* dP, bf16* dS, int T, int Tp8,
+                              long long n_rows, hipStream_t stream) {
     const dim3 grid((unsigned)((n_rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(64 * ROWS_PER_WG);
-    if (Tp8 <= 1024) hipLaunchKernelGGL(softmax_bwd_rows_kernel<16>, grid, block, 0, stream, P, dP, dS, Tp8, n_rows);
-    else if (Tp8 <= 2048) hipLaunchKernelGGL(softmax_bwd_rows_kernel<32>, grid, block, 0, stream, P, dP, dS, Tp8, n_rows);
-    else hipLaunchKernelGGL(softmax_bwd_rows_kernel<64>, grid, block, 0, stream, P, dP, dS, Tp8, n_rows);
+    if (Tp8 <= 1024) hipLaunchKernelGGL(softmax_bwd_rows_kernel<16>, grid, block, 0, stream, P, dP, dS, T, Tp8, n_rows);
+    else if (Tp8 <= 2048) hipLaunchKernelGGL(softmax_bwd_rows_kernel<32>, grid, block, 0, stream, P, dP, dS, T, Tp8, n_rows);
+    else hipLaunchKernelGGL(softmax_bwd_rows_kernel<64>, grid, block, 0, stream, P, dP, dS, T, Tp8, n_rows);
     return hipGetLastError();
 }
 
@@ -434,7 +441,7 @@ hipError_t launch_attn_bwd_unfused_bf16(const void* dout_v, const void* qkv_v, c
     hipError_t e = gemm<OP_ROW, OP_ROW, 128, true>(g, v, Output{dP, H * TT, TT, Tp8}, T, T,
                                                    HEAD_DIM, BH, H, 1.0f, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_softmax_bwd(P, dP, dS, Tp8, (long long)BH * T, stream)) != hipSuccess)
+    if ((e = launch_softmax_bwd(P, dP, dS, T, Tp8, (long long)BH * T, stream)) != hipSuccess)
         return e;
     // dQ = scale dS K: A = dS (rows q, k = key), B = K stored (key, d): tr.
     if ((e = gemm<OP_ROW, OP_TR, 64, false>(ds, k, Output{dqkv, T * rs, HEAD_DIM, rs}, T, HEAD_DIM,

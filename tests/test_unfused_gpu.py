@@ -31,7 +31,11 @@ def run_unfused(qd, gd, H):
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     probs = torch.empty((B, H, T, binding.unfused_row_stride(T)), dtype=torch.bfloat16,
                         device="cuda")
-    ws = torch.empty(binding.unfused_workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    # Every workspace byte 0xff (a NaN in every float): a kernel that reads a
+    # workspace element its producer never wrote (the padding columns of S and
+    # dP when T % 8 != 0) turns the whole row into NaN instead of passing by luck.
+    ws = torch.full((binding.unfused_workspace_bytes(B, T, H),), 255, dtype=torch.uint8,
+                    device="cuda")
     dqkv = torch.full_like(qd, float("nan"))
     binding.attn_fwd_unfused(qd, out, lse, probs, ws, H)
     binding.attn_bwd_unfused(gd, qd, probs, dqkv, ws, H)
@@ -58,6 +62,7 @@ def _check(B, T, H, seed, heads=None, label="unfused"):
 
 
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 2, 1), (1, 64, 2), (1, 65, 1), (2, 200, 3),
+                                   (2, 485, 3),
                                    (3, 129, 2), (1, 1000, 2), (2, 257, 25), (1, 2047, 1),
                                    (1, 4096, 1)])
 def test_unfused_parity(B, T, H):
