@@ -45,10 +45,21 @@ def to_host64(t) -> np.ndarray:
 
 
 def run_library(qkv_dev, dout_dev, n_head: int):
-    """One forward and one backward through the C ABI; returns device tensors."""
+    """One forward and one backward through the C ABI; returns device tensors.
+    The outputs and the backward workspace start as NaN, so an element a
+    kernel leaves unwritten, or a workspace element read before it is
+    written, shows up as a non-finite result instead of passing by luck."""
     import torch
-    out, lse = binding.forward(qkv_dev, n_head)
-    dqkv = binding.backward(dout_dev, qkv_dev, out, lse, n_head)
+    B, T, C3 = (int(x) for x in qkv_dev.shape)
+    C = C3 // 3
+    nan = float("nan")
+    out = torch.full((B, T, C), nan, dtype=qkv_dev.dtype, device=qkv_dev.device)
+    lse = torch.full((B, n_head, T), nan, dtype=torch.float32, device=qkv_dev.device)
+    dqkv = torch.full_like(qkv_dev, nan)
+    ws = torch.full((max(1, binding.workspace_floats(B, T, n_head)),), nan, dtype=torch.float32,
+                    device=qkv_dev.device)
+    binding.attn_fwd(qkv_dev, out, lse, n_head)  # bf16 or float32 by the tensors' dtype
+    binding.attn_bwd(dout_dev, qkv_dev, out, lse, dqkv, ws, n_head)
     torch.cuda.synchronize()
     return out, lse, dqkv
 
