@@ -4,7 +4,8 @@ fp32 and FP8 paths against the same oracles and bars as the other parity
 tests (bf16: max-abs 1e-2 on O, 1e-3 on LSE, rel-L2 2e-2 on dQ, dK, dV;
 fp32: 1e-5 relative; FP8: the bounds of its forward test and rel-L2 2e-2 on
 its gradients against the FP8 oracle), and one larger shape whose outputs
-reach magnitude 4, where O is held to the magnitude-relative bar."""
+reach magnitude 4, where O is held to the magnitude-relative bar, and one
+16384-token sequence."""
 
 import numpy as np
 import pytest
@@ -74,3 +75,9 @@ def test_wide_layer_fp8():
 def test_large_output_shape():
     _check_case(2, 1613, 5, "bf16", 1.0, 0.01, seed=10254, label="large outputs", stress=True,
                 heads=[(0, 0), (0, 4), (1, 2)])
+
+
+# A long sequence, four times the longest workload: one head of 16384 tokens
+# (the oracle holds its 16384 x 16384 float64 matrices, about 2 GB each).
+def test_long_sequence():
+    _check_case(1, 16384, 1, "bf16", 1.0, 0.01, seed=86384, label="long sequence", stress=True)
