@@ -15,9 +15,17 @@
 // The dK/dV and dQ kernels each own disjoint output rows, so the backward
 // uses no atomics and is bitwise reproducible run to run.
 //
-// Workspace (float32, per (batch, head) row padded to Tp = round_up(T, 64)):
-//   ws[0 .. BH*Tp)       D,            0 for t >= T
-//   ws[BH*Tp .. 2*BH*Tp) LSE * log2 e, +inf for t >= T (so P = 0 there)
+// Workspace (float32, per (batch, head) row padded to Tp = round_up(T, 64);
+// 10 * BH * Tp floats in all):
+//   ws[0 .. BH*Tp)        D,            0 for t >= T
+//   ws[BH*Tp .. 2*BH*Tp)  LSE * log2 e, +inf for t >= T (so P = 0 there)
+//   ws[2*BH*Tp .. )       the dK/dV kernel's extra MFMA k-step operands, 32
+//                         bytes per row: for 8 * LSE and for D, three bf16
+//                         values whose sum is the float exactly, then five
+//                         zeros (mfma_terms). Per group of 32 rows the 32
+//                         rows' LSE terms come first, then their D terms
+//                         (term_m, term_d); padding rows take terms that make
+//                         P = 0 (mfma_terms_pad)
 #include <type_traits>
 
 #include "attn_common.h"
