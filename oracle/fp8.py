@@ -353,7 +353,7 @@ def _e4m3_neighbours(x: np.ndarray):
     return lo, hi
 
 
-def rounding_slack(parts: dict, dot_rel_err: float = 2.0 ** -13, x_rel_err: float = 2.0 ** -20):
+def rounding_slack(parts: dict, dot_max_err: float = 2.0 ** -11, x_rel_err: float = 2.0 ** -20):
     """Per-row bounds on what a streaming kernel may legitimately differ from
     head_forward_fp8 by, through the two cases named in the module docstring:
     (a) probabilities 2^(z - m) below 2^-13, whose codes depend on the
@@ -361,8 +361,10 @@ def rounding_slack(parts: dict, dot_rel_err: float = 2.0 ** -13, x_rel_err: floa
     rescale), and (b) codes whose argument x = 2^(z - m + 8) lies within the
     kernel's error of x from a rounding midpoint (each may move by one grid
     step). That error is taken as a dot-product error of at most
-    ``dot_rel_err`` * sum_c |Q^_ic K^_jc| (the sum of the magnitudes of the
-    exact products), which moves z by that / sqrt(d) * log2(e) and x by ln 2
+    ``dot_max_err`` * max_c |Q^_ic K^_jc| (the largest magnitude among the
+    exact products: a matrix unit that aligns its products to the largest one
+    before adding them loses bits in proportion to it, however small the
+    others are), which moves z by that / sqrt(d) * log2(e) and x by ln 2
     times as much, relatively, plus ``x_rel_err`` for the scale, one fused
     multiply-add and exp2 in float32.
 
@@ -380,8 +382,11 @@ def rounding_slack(parts: dict, dot_rel_err: float = 2.0 ** -13, x_rel_err: floa
     xs = np.where(live, np.minimum(x, E4M3_MAX), 1.0)
     lo, hi = _e4m3_neighbours(xs)
     mid = 0.5 * (lo + hi)
-    dot_abs = np.abs(parts["q"]) @ np.abs(parts["k"]).T
-    rel = dot_rel_err * dot_abs / math.sqrt(d) + x_rel_err   # ln 2 * log2(e) = 1
+    qa, ka = np.abs(parts["q"]), np.abs(parts["k"])
+    dot_max = np.empty((qa.shape[0], ka.shape[0]))
+    for r0 in range(0, qa.shape[0], 64):
+        dot_max[r0:r0 + 64] = (qa[r0:r0 + 64, None, :] * ka[None, :, :]).max(axis=2)
+    rel = dot_max_err * dot_max / math.sqrt(d) + x_rel_err   # ln 2 * log2(e) = 1
     if np.any(live & (rel > 2.0 ** -6)):
         # A logit error that large can move a code by several grid steps and
         # the row reference by more than one: the bound below would not hold.

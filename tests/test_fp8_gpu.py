@@ -9,12 +9,14 @@ oracle.fp8.rounding_slack: what a streaming kernel may legitimately move
 product's error of an E4M3 rounding midpoint).
 
 The scaled FP8 MFMA of gfx950 does not sum its 64 exact products in full
-float32: an in-bounds measurement over 2^21 outputs of random E4M3 operands
-found errors up to 2^-13.7 (median 2^-17.7) of the sum of the products'
-magnitudes, where the bf16 MFMA stays within 2^-23. The bound used here is
-2^-13 of that sum per product (ACC_EPS): on the logits through
-rounding_slack, and on O and LSE (whose sums run through the same MFMA) as
-2^-12 of max|V^| and 2^-12 absolute.
+float32. An in-bounds measurement over 2^21 outputs of random E4M3 operands
+found errors up to 2^-13.7 of the sum of the products' magnitudes and up to
+2^-11.2 of the largest product; a wide-range row (one weight of 0.56 beside
+four of about 1e-4) reached 2^-11.5 of its largest product and 2^-11.5 of
+its sum, so the sum is not the right scale. The bound used here is 2^-11 of
+the largest product (ACC_MAX): on the logits through rounding_slack, on the
+row sum (2^-11 relative, so LSE within 2 * 2^-11) and on P V (O within
+4 * 2^-11 of max|V^|, which also covers the row sum's share).
 """
 
 import numpy as np
@@ -30,7 +32,7 @@ from helpers import log, sample_heads, to_device, to_host64
 pytestmark = pytest.mark.gpu
 
 D = 64
-ACC_EPS = 2.0 ** -13
+ACC_MAX = 2.0 ** -11
 
 
 def _unpack(buf: np.ndarray, B: int, T: int, H: int):
@@ -80,7 +82,7 @@ def _check_quantization(host_buf, qkv64, B, T, H, heads):
 
 
 def _check_forward(out, lse, qkv64, H, heads, tag):
-    """Per-row bound (rigorous given ACC_EPS) plus an aggregate gate: the
+    """Per-row bound (rigorous given ACC_MAX) plus an aggregate gate: the
     kernel-minus-oracle difference of O stays below 1% of O in relative L2, so
     that borderline codes cannot hide a systematic error behind the bound."""
     worst_o = worst_l = 0.0
@@ -89,19 +91,21 @@ def _check_forward(out, lse, qkv64, H, heads, tag):
     for b, h in heads:
         qq, kk, vv = oracle.split_packed_head(qkv64, b, h, H, D)
         o_ref, l_ref, parts = F.head_forward_fp8(qq, kk, vv, return_parts=True)
-        o_slack, l_slack = F.rounding_slack(parts, dot_rel_err=ACC_EPS)
+        o_slack, l_slack = F.rounding_slack(parts, dot_max_err=ACC_MAX)
         slack_rows += int((o_slack > 0).sum())
         o = out[b, :, h * D:(h + 1) * D]
         vmax = float(np.abs(parts["v"]).max())
-        base = 2.0 ** -8 * np.abs(o_ref) + 2 * ACC_EPS * vmax
+        base = 2.0 ** -8 * np.abs(o_ref) + 4 * ACC_MAX * vmax
         o_bound = base + o_slack[:, None]
         err = np.abs(o - o_ref)
         bad = np.argwhere(err > o_bound)
         assert len(bad) == 0, (f"{tag} head {b, h}: O off at rows/channels {bad[:5].tolist()}, "
                                f"err {err[tuple(bad[0])]:.3e} bound {o_bound[tuple(bad[0])]:.3e}")
         l_err = np.abs(lse[b, h] - l_ref)
-        l_bound = 2 * ACC_EPS + 2e-6 * np.abs(l_ref) + l_slack
-        assert np.all(l_err <= l_bound), f"{tag} head {b, h}: LSE off by {l_err.max():.3e}"
+        l_bound = 2 * ACC_MAX + 2e-6 * np.abs(l_ref) + l_slack
+        worst = int(np.argmax(l_err - l_bound))
+        assert np.all(l_err <= l_bound), (f"{tag} head {b, h}: LSE off by {l_err[worst]:.3e} at row "
+                                          f"{worst}, bound {l_bound[worst]:.3e}")
         worst_o = max(worst_o, float((err / base).max()))
         worst_l = max(worst_l, float(l_err.max()))
         diff2 += float((err ** 2).sum())
@@ -171,6 +175,21 @@ def test_fp8_forward_wide_range():
     torch.cuda.synchronize()
     _check_forward(to_host64(out), to_host64(lse), I.to_float64(qkv, "bf16"), H,
                    [(0, 0), (0, 1)], "wide range")
+
+
+def test_fp8_forward_wide_range_dominant_weight():
+    """Wide-range rows where one weight dominates the rest by 2^12 (row 4 of
+    head (0, 0): 0.56 beside four weights near 1e-4). The matrix unit's row
+    sum then errs by 2^-11.5 of its largest term, outside a bound scaled by
+    the sum of magnitudes: the case behind the largest-product model."""
+    import torch
+    B, T, H = 2, 300, 4
+    log(f"[case] fp8 forward wide range, dominant weight B={B} T={T} H={H}")
+    qkv = _wide_range(B, T, H, seed=90016, qk_top=2)
+    out, lse = binding.forward_fp8(to_device(qkv, "bf16"), H)
+    torch.cuda.synchronize()
+    _check_forward(to_host64(out), to_host64(lse), I.to_float64(qkv, "bf16"), H,
+                   [(b, h) for b in range(B) for h in range(H)], "wide range, dominant weight")
 
 
 def test_fp8_headline_sampled():
