@@ -1,4 +1,6 @@
-"""The flat bf16 bar on O (max-abs 1e-2) and output magnitude (no GPU).
+"""Where the workloads' bars stop holding for any implementation (no GPU):
+the flat bf16 bar on O against output magnitude, and the fp32 bar against
+logit size.
 
 A bf16 value of magnitude in [4, 8) is a multiple of 2^-5, so even the
 correctly rounded exact output can lie 2^-6 = 0.0156 from it. The
@@ -36,3 +38,34 @@ def test_correctly_rounded_bf16_output_misses_the_flat_bar():
     assert err[t, d] > 1e-2           # the flat bar is out of reach here ...
     assert err[t, d] <= 2.0 ** -6     # ... by at most half a bf16 step at this magnitude
     assert err[t, d] <= 2.0 ** -7 * np.abs(o).max()  # and within the relative bar
+
+
+def test_plain_fp32_misses_the_fp32_bar_at_large_logits():
+    """The fp32 bar 1e-5 * max|ref| is the tiny workload's; it does not hold
+    for logits far beyond the workloads'. With Q and K scaled by 4 (B=1,
+    T=600, 3 heads, seed 80011; logits up to about 87), a straightforward
+    float32 backward misses it on dQ, since the logits' own float32 rounding
+    grows with their size. No committed fp32 GPU test uses such inputs."""
+    import oracle
+    from test_parity_gpu import _scale_qk
+    B, T, H = 1, 600, 3
+    qkv, dout = I.attention_inputs(B, T, H, D, "f32", 1.0, 1.0, seed=80011)
+    qkv = _scale_qk(qkv, "f32", H, 4.0)
+    q64, g64 = I.to_float64(qkv, "f32"), I.to_float64(dout, "f32")
+    ref = oracle.backward_packed(g64, q64, H, D)
+    C = H * D
+    f32 = np.float32
+    worst, refmax = 0.0, float(np.abs(ref[0, :, :C]).max())
+    mask = np.triu(np.ones((T, T), bool), 1)
+    for h in range(H):
+        q, k, v = (q64[0, :, o + h * D:o + (h + 1) * D].astype(f32) for o in (0, C, 2 * C))
+        g = g64[0, :, h * D:(h + 1) * D].astype(f32)
+        s = (q @ k.T) * f32(0.125)
+        s[mask] = -np.inf
+        p = np.exp(s - s.max(1, keepdims=True))
+        p = (p / p.sum(1, keepdims=True)).astype(f32)
+        o = p @ v
+        ds = p * (g @ v.T - (g * o).sum(1, keepdims=True))
+        dq = (ds @ k) * f32(0.125)
+        worst = max(worst, float(np.abs(dq - ref[0, :, h * D:(h + 1) * D]).max()))
+    assert worst > 1e-5 * refmax
