@@ -31,7 +31,10 @@ cache); ``hbm`` is the step's algorithmic HBM rate; ``b64`` times the same
 step at batch 64 and ``other_shapes`` at the 16-head and T = 2048 shapes;
 ``peaks`` measures the chip's sustained bf16 MFMA rate (and
 the clock it ran at) and its HBM copy rate with the library's probes, next to
-the specification peaks the roofline uses.
+the specification peaks the roofline uses; they run before the warm-up steps,
+so the chip has reached its sustained clocks when the timed region starts.
+``tiny_f32`` times the float32 workload (launch-bound; reported only), and
+``cpu_baseline.per_workload`` times the float64 oracle on every workload.
 """
 
 from __future__ import annotations
@@ -96,6 +99,8 @@ def parse_args(argv=None):
                    help="skip the steps after a cache-clearing scratch write")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA and HBM peak probes")
+    p.add_argument("--cpu-seconds-each", type=float, default=8.0,
+                   help="seconds of the float64 oracle per workload in cpu_baseline.per_workload")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -409,10 +414,68 @@ def cpu_baseline(w, target_s: float):
                   f"float64 forward+backward materialising T x T per head, {el:.1f} s wall, "
                   f"counted 7*T^2*d FLOPs per head",
         "wall_s": el,
+        "heads_timed": done,
         "cpu_model": model,
         "cpu_count": os.cpu_count(),
         "affinity_cpus": affinity,
     }
+
+
+def cpu_baseline_all(target_s: float):
+    """The float64 oracle on every workload: whole heads of each, up to about
+    target_s seconds per workload (the whole workload when it fits)."""
+    from causal_flash_attention_amd.workloads import WORKLOADS
+
+    res = {}
+    for wl in WORKLOADS:
+        r = cpu_baseline(wl, target_s)
+        heads_total = wl.B * wl.n_head
+        heads_done = r["heads_timed"]
+        res[wl.name] = {"dtype": wl.dtype, "heads_timed": heads_done, "heads_total": heads_total,
+                        "wall_s": r["wall_s"], "counted_gflops": 1000.0 * r["value"],
+                        "est_whole_workload_s": r["wall_s"] * heads_total / heads_done,
+                        "blas_threads": r["cores"]}
+    return res
+
+
+def time_tiny_f32(stream, dev, n=200):
+    """The float32 workload (B 1, T 64, 2 heads): attn_fwd_f32 + attn_bwd_f32
+    per step, n steps between HIP events. At this size a step is a few
+    launches' worth of latency, so the time is reported, not judged."""
+    import numpy as np
+    import torch
+
+    from causal_flash_attention_amd import binding
+    from causal_flash_attention_amd import inputs as I
+    from causal_flash_attention_amd.workloads import BY_NAME
+
+    w = BY_NAME["tiny_f32_b1_h2_t64"]
+    B, T, H, D = w.B, w.T, w.n_head, w.head_dim
+    qh, gh = I.attention_inputs(B, T, H, D, "f32", w.qkv_std, w.dout_std, seed=0)
+    qkv = torch.from_numpy(np.ascontiguousarray(qh, dtype=np.float32)).to(dev)
+    dout = torch.from_numpy(np.ascontiguousarray(gh, dtype=np.float32)).to(dev)
+    out = torch.empty((B, T, H * D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dqkv = torch.empty_like(qkv)
+    delta = torch.empty(binding.workspace_floats(B, T, H), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.attn_fwd(qkv, out, lse, H, D, stream)
+        binding.attn_bwd(dout, qkv, out, lse, dqkv, delta, H, D, stream)
+
+    for _ in range(20):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / n
+    return {"workload": w.name, "dtype": "f32", "us_per_step": us, "steps": n,
+            "counted_gflops": w.counted_flops()["total"] / (us * 1e-6) / 1e9,
+            "what": "launch-bound: time reported only, not judged against a roofline"}
 
 
 def step_hbm_bytes(w) -> float:
@@ -818,6 +881,14 @@ def main(argv=None):
               "attn_bwd_dkdv": lambda: binding.attn_bwd_dkdv(dout, qkv, delta, dqkv, H, D, stream)}
     assert list(stages) == STAGES
 
+    # The chip's sustained peaks are measured first: about a second of full
+    # load, which also brings the clocks to where they stay under sustained
+    # load. After idle, the first tens of milliseconds of load run up to 25%
+    # slower (measured: 203.8 against 162.9 us per step on one box with 5
+    # and 200 warm-up steps), which would otherwise leak into a short timed
+    # region.
+    peaks = None if args.no_peaks else measure_peaks(stream, dev)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -887,7 +958,7 @@ def main(argv=None):
     others = None if args.no_b64 else {
         n: time_other_batch(BY_NAME[n], stream, dev, min(K, 50))
         for n in ("gpt2_350m_b16_t1024", "gpt2_1p5b_style_b4_t2048_h25")}
-    peaks = None if args.no_peaks else measure_peaks(stream, dev)
+    tiny = None if args.no_b64 else time_tiny_f32(stream, dev)
 
     unfused = None if args.no_unfused else time_unfused(w, qkv, dout, stream, K)
     decode = None if args.no_decode else time_decode(stream)
@@ -943,6 +1014,8 @@ def main(argv=None):
         result["b64"] = b64
     if others is not None:
         result["other_shapes"] = others
+    if tiny is not None:
+        result["tiny_f32"] = tiny
     if unfused is not None:
         unfused["fa_speedup"] = unfused["ms_per_step"] / ms_per_step
         result["unfused"] = unfused
@@ -954,6 +1027,7 @@ def main(argv=None):
         result["block"] = block
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"]["per_workload"] = cpu_baseline_all(args.cpu_seconds_each)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -10,6 +10,7 @@ runs in the library's HIP kernels; there is no fallback. ``forward`` and
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -466,17 +467,28 @@ def attn_version() -> int:
 
 
 # ---------------------------------------------------------------------------
-# Allocating conveniences.
+# Allocating conveniences. With an explicit `stream`, the outputs and every
+# scratch buffer are allocated while that stream is torch's current stream,
+# so the caching allocator ties their memory to it: a scratch buffer dropped
+# on return is handed out again only to work ordered after these kernels on
+# the same stream. The outputs belong to `stream` in the same way; a caller
+# that reads them on another stream orders the two streams first, as with
+# any torch tensor.
 # ---------------------------------------------------------------------------
+
+def _on(stream):
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
 
 def forward(qkv, n_head: int, head_dim: int = 64, stream=None):
     """Returns (out, lse) for a packed (B, T, 3C) bf16 or fp32 GPU tensor."""
-    torch = _torch()
-    B, T, C = _dims(qkv, n_head, head_dim)
-    out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
-    lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
-    attn_fwd(qkv, out, lse, n_head, head_dim, stream)
-    return out, lse
+    with _on(stream):
+        torch = _torch()
+        B, T, C = _dims(qkv, n_head, head_dim)
+        out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
+        lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+        attn_fwd(qkv, out, lse, n_head, head_dim, stream)
+        return out, lse
 
 
 def fp8_bwd_buffer_bytes(B: int, T: int, n_head: int) -> int:
@@ -517,35 +529,38 @@ def backward_fp8(dout, qkv, out, lse, n_head: int, head_dim: int = 64, stream=No
     """dqkv of the FP8 backward for the FP8 forward that produced (out, lse)
     on qkv: quantize the forward and backward operands into new buffers, then
     attn_bwd_fp8."""
-    torch = _torch()
-    B, T, C = _dims(qkv, n_head, head_dim)
-    f8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
-    b8 = torch.empty(fp8_bwd_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
-    dqkv = torch.empty_like(qkv)
-    attn_quantize_fp8(qkv, f8, n_head, head_dim, stream)
-    attn_quantize_bwd_fp8(dout, qkv, out, lse, b8, n_head, head_dim, stream)
-    attn_bwd_fp8(f8, b8, dqkv, n_head, head_dim, stream)
-    return dqkv
+    with _on(stream):
+        torch = _torch()
+        B, T, C = _dims(qkv, n_head, head_dim)
+        f8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+        b8 = torch.empty(fp8_bwd_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+        dqkv = torch.empty_like(qkv)
+        attn_quantize_fp8(qkv, f8, n_head, head_dim, stream)
+        attn_quantize_bwd_fp8(dout, qkv, out, lse, b8, n_head, head_dim, stream)
+        attn_bwd_fp8(f8, b8, dqkv, n_head, head_dim, stream)
+        return dqkv
 
 
 def forward_fp8(qkv, n_head: int, head_dim: int = 64, stream=None):
     """Returns (out, lse) of the FP8 forward for a packed (B, T, 3C) bf16 GPU
     tensor: attn_quantize_fp8 into a new buffer, then attn_fwd_fp8."""
-    torch = _torch()
-    B, T, C = _dims(qkv, n_head, head_dim)
-    fp8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
-    out = torch.empty((B, T, C), dtype=torch.bfloat16, device=qkv.device)
-    lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
-    attn_quantize_fp8(qkv, fp8, n_head, head_dim, stream)
-    attn_fwd_fp8(fp8, out, lse, n_head, head_dim, stream)
-    return out, lse
+    with _on(stream):
+        torch = _torch()
+        B, T, C = _dims(qkv, n_head, head_dim)
+        fp8 = torch.empty(fp8_buffer_bytes(B, T, n_head), dtype=torch.uint8, device=qkv.device)
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=qkv.device)
+        lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+        attn_quantize_fp8(qkv, fp8, n_head, head_dim, stream)
+        attn_fwd_fp8(fp8, out, lse, n_head, head_dim, stream)
+        return out, lse
 
 
 def backward(dout, qkv, out, lse, n_head: int, head_dim: int = 64, stream=None):
     """Returns dqkv (B, T, 3C) for the forward that produced (out, lse)."""
-    torch = _torch()
-    B, T, C = _dims(qkv, n_head, head_dim)
-    dqkv = torch.empty_like(qkv)
-    delta = torch.empty(workspace_floats(B, T, n_head), dtype=torch.float32, device=qkv.device)
-    attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
-    return dqkv
+    with _on(stream):
+        torch = _torch()
+        B, T, C = _dims(qkv, n_head, head_dim)
+        dqkv = torch.empty_like(qkv)
+        delta = torch.empty(workspace_floats(B, T, n_head), dtype=torch.float32, device=qkv.device)
+        attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
+        return dqkv

@@ -5,8 +5,12 @@ The backward buffer is integer work plus two float rows: every code and
 exponent byte (padding included) must equal the oracle's quantization bit for
 bit; LSE * log2(e) must equal its float32 product exactly; D must match its
 float64 value to float32 rounding. The gradients are compared with
-oracle.fp8.head_backward_fp8 fed the GPU forward's own O and LSE, at the
-attention backward's bar (relative L2 <= 2e-2 on each of dQ, dK, dV): the
+oracle.fp8.head_backward_fp8 at the attention backward's bar (relative L2
+<= 2e-2 on each of dQ, dK, dV). Both sides take the same forward results,
+made by the oracle alone: the FP8 oracle's O rounded to bf16 and its LSE
+rounded to float32, so no input of the oracle comes from the GPU (heads that
+are not compared take the GPU forward's values, as inputs of the GPU
+backward only). The
 kernel's probabilities and dS differ from the oracle's only by the FP8
 matrix cores' accumulation (about 14 bits) and float32 arithmetic, which can
 move single E4M3 codes across a rounding midpoint, not by any rounding of
@@ -78,13 +82,40 @@ def _check_grads(dqkv, qkv64, dout64, out64, lse64, H, heads, tag):
     return rel
 
 
-def _run_bwd(qkv, dout, B, T, H, std_tag):
+def _oracle_forward(qkv, qd, B, T, H, heads):
+    """O (bf16 bits) and LSE (float32) for the backward: the FP8 oracle's
+    forward on the listed heads; the other heads (never compared) keep the
+    GPU forward's values."""
     import torch
+    q64 = I.to_float64(qkv, "bf16")
+    if len(heads) < B * H:
+        out_d, lse_d = _forward(qd, H)
+        out_bits = out_d.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+        lse32 = lse_d.cpu().numpy().copy()
+    else:
+        out_bits = np.zeros((B, T, H * D), dtype=np.uint16)
+        lse32 = np.zeros((B, H, T), dtype=np.float32)
+    ref_o, ref_l = F.forward_packed_fp8(q64, H, D, heads=heads)
+    for b, h in heads:
+        sl = slice(h * D, (h + 1) * D)
+        out_bits[b, :, sl] = I.f32_to_bf16_bits(ref_o[b, :, sl].astype(np.float32))
+        lse32[b, h] = ref_l[b, h].astype(np.float32)
+    return out_bits, lse32
+
+
+def _run_bwd(qkv, dout, B, T, H, heads=None):
+    """GPU FP8 backward on the oracle's forward results; returns the float64
+    O and LSE both sides use and the GPU's dqkv."""
+    import torch
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
     qd, gd = to_device(qkv, "bf16"), to_device(dout, "bf16")
-    out, lse = _forward(qd, H)
+    out_bits, lse32 = _oracle_forward(qkv, qd, B, T, H, heads)
+    out, lse = to_device(out_bits, "bf16"), torch.from_numpy(lse32).to("cuda")
     dqkv = binding.backward_fp8(gd, qd, out, lse, H)
     torch.cuda.synchronize()
-    return to_host64(out), to_host64(lse), to_host64(dqkv), (qd, gd, out, lse)
+    o64 = I.bf16_bits_to_f32(out_bits).astype(np.float64)
+    return o64, lse32.astype(np.float64), to_host64(dqkv), (qd, gd, out, lse)
 
 
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 63, 2), (2, 65, 3), (1, 200, 2)])
@@ -94,13 +125,14 @@ def test_fp8_bwd_buffer(B, T, H):
     log(f"[case] fp8 bwd buffer B={B} T={T} H={H}")
     qkv, dout = _inputs(B, T, H, 1.0, 2100 + T)
     qd, gd = to_device(qkv, "bf16"), to_device(dout, "bf16")
-    out, lse = _forward(qd, H)
+    out_bits, lse32 = _oracle_forward(qkv, qd, B, T, H, [(b, h) for b in range(B) for h in range(H)])
+    out, lse = to_device(out_bits, "bf16"), torch.from_numpy(lse32).to("cuda")
     buf = torch.full((binding.fp8_bwd_buffer_bytes(B, T, H),), 0xAB, dtype=torch.uint8, device="cuda")
     binding.attn_quantize_bwd_fp8(gd, qd, out, lse, buf, H)
     torch.cuda.synchronize()
     vc, gc, qp, kp, gp, ex, lse2, dd = _unpack_bwd(buf.cpu().numpy(), B, T, H)
-    q64, g64, o64 = I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), to_host64(out)
-    lse32 = lse.cpu().numpy()
+    q64, g64 = I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16")
+    o64 = I.bf16_bits_to_f32(out_bits).astype(np.float64)
     C = H * D
     T32 = -(-T // 32) * 32
     for b in range(B):
@@ -133,7 +165,7 @@ def test_fp8_bwd_buffer(B, T, H):
 def test_fp8_bwd_parity(B, T, H, std):
     log(f"[case] fp8 bwd B={B} T={T} H={H} std={std}")
     qkv, dout = _inputs(B, T, H, std, 2300 + T)
-    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, std)
+    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H)
     _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
                  [(b, h) for b in range(B) for h in range(H)], f"B={B} T={T} H={H} std={std}")
 
@@ -143,18 +175,21 @@ def test_fp8_bwd_headline_sampled():
     B, T, H = 16, 1024, 12
     log(f"[case] fp8 bwd headline B={B} T={T} H={H}")
     qkv, dout = _inputs(B, T, H, 1.0, 2024)
-    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, 1.0)
+    heads = sample_heads(B, H, 4, seed=5)
+    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, heads)
     _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
-                 sample_heads(B, H, 4, seed=5), "headline")
+                 heads, "headline")
 
 
 def test_fp8_bwd_deterministic_and_close_to_exact():
-    """Two runs agree bit for bit; the FP8 gradients stay within about 2^-3
-    (relative L2) of the exact gradients of the unquantized inputs."""
+    """Two runs agree bit for bit; the whole FP8 chain (the GPU's FP8 forward,
+    then its backward) stays within about 2^-3 (relative L2) of the exact
+    gradients of the unquantized inputs."""
     import torch
     B, T, H = 2, 256, 2
     qkv, dout = _inputs(B, T, H, 1.0, 77)
-    _, _, _, (qd, gd, out, lse) = _run_bwd(qkv, dout, B, T, H, 1.0)
+    qd, gd = to_device(qkv, "bf16"), to_device(dout, "bf16")
+    out, lse = _forward(qd, H)
     a = binding.backward_fp8(gd, qd, out, lse, H)
     b = binding.backward_fp8(gd, qd, out, lse, H)
     torch.cuda.synchronize()

@@ -319,6 +319,54 @@ def pin_rounding_slack(M):
     assert abs(ls_[1] - 2.0 ** -17 / (parts["l"][1] - 2.0 ** -17)) < 1e-18
 
 
+def pin_rounding_slack_near_midpoint(M):
+    """Branch (b) of the slack: a code whose argument lies within the
+    kernel's error of an E4M3 rounding midpoint, worked by hand.
+
+    T = 2, only channels 0 and 1 non-zero: q_0 = 0, q_1 = (1, 1);
+    k_0 = (0.3125, -22), k_1 = 0; v_0 = (1, 0, ...), v_1 = 0. Every value has
+    at most four significant bits, so each MX block holds it exactly
+    (k_0's block takes e = -4: 5 and -352 are E4M3 codes).
+
+    Row 1: z_11 = 0 and z_10 = (0.3125 - 22) log2(e) / 8 = -3.9115, so the
+    reference is m_1 = ceil(0) = 0 and the arguments 2^(z - m + 8) are
+    x_11 = 256 (a grid value) and x_10 = 17.01746, just above the midpoint 17
+    between the E4M3 neighbours 16 and 18 (it rounds to 18: P^_10 = 18/256,
+    l_1 = 274/256). The pair's largest product is |k_0,1 q_1,1| = 22, so the
+    allowed relative error of x is 2^-11 * 22 / 8 + 2^-20 = 1.3437e-3, and
+    |x_10 - 17| / x_10 = 1.0261e-3 lies inside it: that code may move by one
+    grid step, 2 / 256. With the moved weight w = 2^-7:
+      lse_slack_1 = w / (l_1 - w) = (2/256) / (272/256) = 1/136,
+      O_1 = (18/256 v_0) / l_1 = 18/274 v_0, spread max_c |v_0c - O_1c| =
+      256/274, so o_slack_1 = w * 256/274 / (272/256) = 512 / (274 * 272).
+    Row 0 (one key, x = 256) and code x_11 are on the grid: no slack.
+
+    A second head with k_0 = (0.34375, -22) puts x_10 = 17.08407 at
+    4.92e-3 relative from the midpoint, 3.7 times the allowed error: no
+    slack anywhere. (The earlier sum-scaled model, 2^-13 * 22.3125 / 8, would
+    allow only 3.41e-4 in the first case, and a bound without the 1/sqrt(d)
+    would take in the second.)"""
+    d = 64
+
+    def slack(k01):
+        q = np.zeros((2, d))
+        k = np.zeros((2, d))
+        v = np.zeros((2, d))
+        q[1, 0] = q[1, 1] = 1.0
+        k[0, 0], k[0, 1] = k01, -22.0
+        v[0, 0] = 1.0
+        _, _, parts = M.head_forward_fp8(q, k, v, return_parts=True)
+        assert parts["p_hat"][1, 0] == 18.0 / 256.0 and parts["p_hat"][1, 1] == 1.0
+        return M.rounding_slack(parts)
+
+    os_, ls_ = slack(0.3125)
+    assert os_[0] == 0 and ls_[0] == 0
+    assert abs(ls_[1] - 1.0 / 136.0) <= 1e-15
+    assert abs(os_[1] - 512.0 / (274.0 * 272.0)) <= 1e-15
+    os_, ls_ = slack(0.34375)
+    assert np.all(os_ == 0) and np.all(ls_ == 0)
+
+
 def _brute_backward(q, k, v, g, o, lse):
     """FP8 backward steps B1-B6 in pure-Python loops from the brute-force
     quantizers."""
@@ -427,6 +475,7 @@ PINS = [
     pin_near_exact_attention,
     pin_packed_layout,
     pin_rounding_slack,
+    pin_rounding_slack_near_midpoint,
     pin_backward_brute_force,
     pin_backward_zero_upstream,
     pin_backward_near_exact,
@@ -444,7 +493,26 @@ def test_fp8_oracle_pin(pin):
 
 _orig = {name: getattr(F, name) for name in
          ("e4m3_decode", "e4m3_encode", "mx_scale_exponent", "quantize_head", "_logits",
-          "_probabilities", "head_forward_fp8")}
+          "_probabilities", "head_forward_fp8", "_dot_error_bound", "_e4m3_neighbours")}
+
+
+def _dot_error_sum_scaled(q, k, dot_max_err):
+    """The slack's earlier error model: 2^-13 of the sum of the products'
+    magnitudes."""
+    return 2.0 ** -13 * (np.abs(q) @ np.abs(k).T)
+
+
+def _dot_error_no_sqrt_d(q, k, dot_max_err):
+    """The right bound on the dot product taken as the bound on the logit
+    (the 1/sqrt(d) forgotten)."""
+    return _orig["_dot_error_bound"](q, k, dot_max_err) * math.sqrt(q.shape[1])
+
+
+def _neighbours_from_code(x):
+    """The grid neighbours taken as the rounded value and the next one up,
+    whichever side of x the rounded value lies."""
+    code = F.e4m3_encode(x).astype(np.int64)
+    return F.e4m3_decode(code), F.e4m3_decode(np.minimum(code + 1, 0x7E))
 
 
 def _decode_bias8(codes):
@@ -584,6 +652,9 @@ MUTANTS = {
     "l_from_unquantized_p": {"head_forward_fp8": _forward_variant("l_unquantized")},
     "lse_natural_m": {"head_forward_fp8": _forward_variant("lse_natural_m")},
     "lse_keeps_2^8": {"head_forward_fp8": _forward_variant("lse_no_shift_undo")},
+    "slack_sum_scaled_error": {"_dot_error_bound": _dot_error_sum_scaled},
+    "slack_without_sqrt_d": {"_dot_error_bound": _dot_error_no_sqrt_d},
+    "slack_wrong_neighbour": {"_e4m3_neighbours": _neighbours_from_code},
 }
 
 

@@ -36,7 +36,7 @@ def _transform(qkv, dtype, fn):
 
 
 def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", qk_gain=1.0,
-                stress=False, transform=None):
+                stress=False, transform=None, f32_flat=False):
     log(f"[case] {label} B={B} T={T} H={H} dtype={dtype} seed={seed} qk_gain={qk_gain}")
     qkv, dout = I.attention_inputs(B, T, H, D, dtype, qkv_std, dout_std, seed=seed)
     if qk_gain != 1.0:
@@ -56,7 +56,7 @@ def _check_case(B, T, H, dtype, qkv_std, dout_std, seed, heads=None, label="", q
     for k in ("out", "lse", "dqkv"):
         assert np.all(np.isfinite(gpu[k])), (label, k)
     o_bound = bf16_o_bound(m["o_refmax"]) if stress else BF16_O_MAXABS
-    assert_parity(m, dtype, f"{label} B={B} T={T} H={H} {dtype}", o_bound)
+    assert_parity(m, dtype, f"{label} B={B} T={T} H={H} {dtype}", o_bound, f32_flat=f32_flat)
     return m
 
 
@@ -70,8 +70,10 @@ def test_workload_parity(w):
         heads = None  # every head
     else:
         heads = sample_heads(w.B, w.n_head, 40, seed=1)
+    # The tiny float32 workload is held to the flat max-abs 1e-5 on every
+    # tensor; the bf16 workloads to 1e-2 on O and 2e-2 relative L2 on dQ, dK, dV.
     _check_case(w.B, w.T, w.n_head, w.dtype, w.qkv_std, w.dout_std, seed=0,
-                heads=heads, label=w.name)
+                heads=heads, label=w.name, f32_flat=(w.dtype == "f32"))
 
 
 # ----------------------------------------------------------------------------

@@ -10,9 +10,10 @@ reach magnitude 4, where O is held to the magnitude-relative bar, and one
 import numpy as np
 import pytest
 
+from causal_flash_attention_amd import binding
 from causal_flash_attention_amd import inputs as I
 
-from helpers import log
+from helpers import log, to_device, to_host64
 from test_fp8_bwd_gpu import _check_grads, _inputs as fp8_inputs, _run_bwd
 from test_fp8_gpu import _check_forward
 from test_parity_gpu import _check_case
@@ -39,11 +40,21 @@ def test_random_shape_f32(B, T, H):
 def test_random_shape_fp8(B, T, H):
     log(f"[case] random shape fp8 B={B} T={T} H={H}")
     qkv, dout = fp8_inputs(B, T, H, 1.0, 7000 + T)
-    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, 1.0)
     heads = [(b, h) for b in range(B) for h in range(H)]
-    _check_forward(out64, lse64, I.to_float64(qkv, "bf16"), H, heads, f"random B={B} T={T} H={H}")
-    _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
-                 heads, f"random B={B} T={T} H={H}")
+    _fp8_forward_and_backward(qkv, dout, B, T, H, heads, f"random B={B} T={T} H={H}")
+
+
+def _fp8_forward_and_backward(qkv, dout, B, T, H, heads, tag):
+    """The GPU FP8 forward against the FP8 oracle; then the GPU FP8 backward,
+    fed the oracle's forward results, against the oracle's backward."""
+    import torch
+    qd = to_device(qkv, "bf16")
+    out, lse = binding.forward_fp8(qd, H)
+    torch.cuda.synchronize()
+    q64 = I.to_float64(qkv, "bf16")
+    _check_forward(to_host64(out), to_host64(lse), q64, H, heads, tag)
+    o64, l64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, heads)
+    _check_grads(dqkv, q64, I.to_float64(dout, "bf16"), o64, l64, H, heads, tag)
 
 
 # A wide layer: 160 heads (C = 10240, a 60 KB packed row), where the tile
@@ -62,11 +73,7 @@ def test_wide_layer_fp8():
     B, T, H = WIDE
     log(f"[case] wide layer fp8 B={B} T={T} H={H}")
     qkv, dout = fp8_inputs(B, T, H, 1.0, 8200)
-    out64, lse64, dqkv, _ = _run_bwd(qkv, dout, B, T, H, 1.0)
-    heads = [(0, h) for h in (0, 1, 77, 158, 159)]
-    _check_forward(out64, lse64, I.to_float64(qkv, "bf16"), H, heads, "wide")
-    _check_grads(dqkv, I.to_float64(qkv, "bf16"), I.to_float64(dout, "bf16"), out64, lse64, H,
-                 heads, "wide")
+    _fp8_forward_and_backward(qkv, dout, B, T, H, [(0, h) for h in (0, 1, 77, 158, 159)], "wide")
 
 
 # A shape whose outputs reach magnitude 4 (query 1 of head (0, 0)). No bf16
