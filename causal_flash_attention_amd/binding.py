@@ -41,6 +41,8 @@ SIGNATURES = {
     "attn_bwd_dkdv": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_dq": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_bwd_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
+    "attn_bwd_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "attn_bwd_noalloc_max_floats": ([], ctypes.c_longlong),
     "attn_unfused_workspace_bytes": ([_I, _I, _I], ctypes.c_longlong),
     "attn_fwd_unfused": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "attn_decode_workspace_floats": ([_I, _I, _I], ctypes.c_longlong),
@@ -184,6 +186,25 @@ def _require_ws(delta, B, T, n_head):
 def attn_bwd(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,
              stream=None) -> None:
     _bwd_full("attn_bwd", dout, qkv, out, lse, dqkv, delta, n_head, head_dim, stream)
+
+
+def attn_bwd_noalloc(dout, qkv, out, lse, dqkv, n_head: int, head_dim: int = 64,
+                     stream=None) -> None:
+    """attn_bwd with the library's own per-GPU workspace (no allocation)."""
+    torch = _torch()
+    if qkv is None or qkv.dtype != torch.bfloat16:
+        raise ValueError("attn_bwd_noalloc takes bfloat16 tensors")
+    B, T, C = _dims(qkv, n_head, head_dim)
+    for t, name, shape in ((dout, "dout", (B, T, C)), (qkv, "qkv", (B, T, 3 * C)),
+                           (out, "out", (B, T, C)), (dqkv, "dqkv", (B, T, 3 * C))):
+        _require(t, name, torch.bfloat16, shape)
+    _require(lse, "lse", torch.float32, (B, n_head, T))
+    _check(lib().attn_bwd_noalloc(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dqkv),
+                                  B, T, n_head, head_dim, _stream_ptr(stream)), "attn_bwd_noalloc")
+
+
+def noalloc_max_floats() -> int:
+    return int(lib().attn_bwd_noalloc_max_floats())
 
 
 def attn_bwd_dq_preprocess(dout, qkv, out, lse, dqkv, delta, n_head: int, head_dim: int = 64,

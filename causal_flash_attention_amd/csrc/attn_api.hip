@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "causal_attn.h"
 
 namespace cattn {
@@ -264,6 +266,51 @@ int bwd_common(const void* dout, const void* qkv, const void* out, const float* 
     return ATTN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The workspace of attn_bwd_noalloc: one file-scope device array, of which
+// every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// its device address is looked up once per device (with that device
+// current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr long long kNoallocWsFloats = 8LL << 20;  // 32 MiB
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) float scratch[kNoallocWsFloats];
+
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream).
+int scratch_for_stream(hipStream_t stream, float** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail_hip(e, "attn_bwd_noalloc: hipGetDevice");
+    int dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return fail_hip(e, "attn_bwd_noalloc: hipStreamGetDevice");
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail_hip(e, "attn_bwd_noalloc: hipSetDevice");
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess && r != hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return fail_hip(e, "attn_bwd_noalloc: hipGetSymbolAddress");
+        if (p == nullptr) return fail(ATTN_ERR_HIP, "attn_bwd_noalloc: no device address");
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 // Extra limits of the materialising path: rows of up to unfused_max_T()
 // keys held in one wave's registers by the row kernels, and one grid row per
 // head in its matrix products.
@@ -322,6 +369,24 @@ int attn_bwd(const void* dout, const void* qkv, const void* out, const float* ls
              float* delta, int B, int T, int n_head, int head_dim, void* stream) {
     return bwd_common(dout, qkv, out, lse, dqkv, delta, B, T, n_head, head_dim, stream, 2, kAll);
 }
+
+int attn_bwd_noalloc(const void* dout, const void* qkv, const void* out, const float* lse,
+                     void* dqkv, int B, int T, int n_head, int head_dim, void* stream) {
+    g_last_error[0] = '\0';
+    if (!(B == 0 || T == 0 || n_head == 0) && (!dout || !qkv || !out || !lse || !dqkv))
+        return fail(ATTN_ERR_NULL_PTR, "attn_bwd_noalloc: a tensor pointer is NULL");
+    bool empty = false;
+    int st = check_shape(B, T, n_head, head_dim, 2, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (workspace_floats(B, T, n_head) > kNoallocWsFloats)
+        return fail(ATTN_ERR_TOO_LARGE, "attn_bwd_noalloc: the workspace of this shape exceeds "
+                                        "attn_bwd_noalloc_max_floats()");
+    float* ws = nullptr;
+    if ((st = scratch_for_stream(as_stream(stream), &ws)) != ATTN_OK) return st;
+    return bwd_common(dout, qkv, out, lse, dqkv, ws, B, T, n_head, head_dim, stream, 2, kAll);
+}
+
+long long attn_bwd_noalloc_max_floats(void) { return kNoallocWsFloats; }
 
 int attn_bwd_preprocess(const void* dout, const void* out, const float* lse, float* delta, int B,
                         int T, int n_head, int head_dim, void* stream) {

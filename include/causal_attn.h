@@ -132,6 +132,24 @@ int attn_bwd_dq(const void* dout, const void* qkv, const float* delta, void* dqk
  * -1 if an argument is negative or the size would pass 2^62 bytes. */
 long long attn_bwd_workspace_floats(int B, int T, int n_head);
 
+/* attn_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same kernels and results as attn_bwd (bit for bit), with the workspace in
+ * an array the library keeps in each GPU's memory until the process ends
+ * (attn_bwd_noalloc_max_floats() floats, 32 MiB) instead of a `delta`
+ * argument; the call itself allocates nothing. Arguments, layouts and
+ * errors as attn_bwd, plus ATTN_ERR_TOO_LARGE when
+ * attn_bwd_workspace_floats(B, T, n_head) exceeds that size (B 64, T 1024,
+ * 12 heads fits). The array is found on the device that runs `stream` (the
+ * current device for NULL); the first call on a device looks its address up.
+ * Every call on one GPU shares that GPU's array: calls ordered on one stream
+ * are safe, calls that may overlap on one GPU (other streams, other threads)
+ * race on it and must not be issued. Nothing in it needs to start at zero:
+ * the first kernel writes every element the second reads. */
+int attn_bwd_noalloc(const void* dout, const void* qkv, const void* out, const float* lse,
+                     void* dqkv, int B, int T, int n_head, int head_dim, void* stream);
+long long attn_bwd_noalloc_max_floats(void);
+
 /* --------------------------------------------------------------- fp32 ---- */
 
 /* Same operations in float32 storage and arithmetic (same workspace). */

@@ -81,6 +81,8 @@ int main(void) {
 #define p(i) ptr(s, i)
                         check(attn_fwd(p(0), p(1), p(2), B, T, H, d, NULL), "attn_fwd");
                         check(attn_bwd(p(0), p(1), p(2), p(3), p(4), p(5), B, T, H, d, NULL), "attn_bwd");
+                        check(attn_bwd_noalloc(p(0), p(1), p(2), p(3), p(4), B, T, H, d, NULL),
+                              "attn_bwd_noalloc");
                         check(attn_bwd_preprocess(p(0), p(1), p(2), p(3), B, T, H, d, NULL), "attn_bwd_preprocess");
                         check(attn_bwd_dq_preprocess(p(0), p(1), p(2), p(3), p(4), p(5), B, T, H, d, NULL),
                               "attn_bwd_dq_preprocess");

@@ -44,6 +44,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_bwd_preprocess",
               "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess", "attn_bwd_workspace_floats",
+              "attn_bwd_noalloc", "attn_bwd_noalloc_max_floats",
               "attn_fwd_unfused", "attn_bwd_unfused", "attn_unfused_workspace_bytes",
               "attn_decode", "attn_decode_workspace_floats",
               "attn_fp8_buffer_bytes", "attn_quantize_fp8", "attn_fwd_fp8",
@@ -297,6 +298,22 @@ def test_workspace_size(L):
     assert L.attn_bwd_workspace_floats(3, 1, 5) == 10 * 3 * 5 * 64
     assert L.attn_bwd_workspace_floats(0, 10, 2) == 0
     assert L.attn_bwd_workspace_floats(-1, 10, 2) == -1
+
+
+@no_gpu_only
+def test_noalloc_validation(L):
+    # Everything below is rejected before the library looks for its
+    # workspace array on a device.
+    assert L.attn_bwd_noalloc_max_floats() == 8 << 20
+    assert L.attn_bwd_noalloc(None, None, None, None, None, 0, 64, 2, 64, None) == 0
+    assert L.attn_bwd_noalloc(G, Q, O, LS, None, 1, 64, 2, 64, None) == -1
+    assert L.attn_bwd_noalloc(G, Q, O, LS, DQ, 1, 64, 2, 32, None) == -3
+    assert L.attn_bwd_noalloc(G, Q, O, LS, DQ, -1, 64, 2, 64, None) == -2
+    # 10 * 64 * 12 * round_up(T, 64) floats: T = 1088 fits, T = 1089 does not.
+    assert L.attn_bwd_workspace_floats(64, 1088, 12) <= L.attn_bwd_noalloc_max_floats()
+    assert L.attn_bwd_workspace_floats(64, 1089, 12) > L.attn_bwd_noalloc_max_floats()
+    assert L.attn_bwd_noalloc(G, Q, O, LS, DQ, 64, 1089, 12, 64, None) == -4
+    assert "attn_bwd_noalloc_max_floats" in L.attn_last_error().decode()
 
 
 def test_empty_problems_are_noops(L):
