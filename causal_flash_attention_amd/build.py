@@ -30,6 +30,8 @@ HIPCC_FLAGS = [
     # which the softmax and rescale would otherwise copy back and forth.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
+    # the hand-scheduled programs clobber m0 on purpose (direct LDS loads)
+    "-Wno-inline-asm",
 ]
 
 
@@ -40,8 +42,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
+# Generators of hand-scheduled kernel programs: each writes an include next
+# to itself (committed, so that the sources build as they stand).
+GENERATORS = ["gen_attn_fwd_asm.py"]
+
+
+def generate() -> None:
+    for gen in GENERATORS:
+        subprocess.run([sys.executable, os.path.join(CSRC, gen)], check=True, capture_output=True)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIB_PATH; returns the path."""
+    """Regenerate the kernel programs, then compile every HIP source into
+    LIB_PATH; returns the path."""
+    generate()
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]

@@ -277,6 +277,84 @@ __global__ __launch_bounds__(256, CATTN_FWD_WAVES_PER_SIMD) void attn_fwd_bf16_k
     }
 }
 
+// The kernel the library launches: the same computation with the wave's
+// whole program scheduled by hand (attn_fwd_asm.inc, written by
+// gen_attn_fwd_asm.py): one inline-asm block per wave, from the Q load to
+// the O and LSE stores. C++ only maps the workgroup to (query tile, head),
+// exactly as above, and hands the program wave-uniform scalars. The program
+// issues one MFMA between every few VALU instructions: the scores of tile
+// j+1 between the exponentials of tile j, P V of tile j between the row sum
+// of j and the row max of j+1. Compiled from the C++ above (build with
+// -DCATTN_FWD_COMPILED), the same schedule waits on each operand read just
+// before its MFMA and runs about 10% slower.
+#include "attn_fwd_asm.inc"
+
+// One (query tile, head) item: the wave's program from the Q load to the O
+// and LSE stores.
+__device__ __forceinline__ void fwd_asm_item(const bf16* __restrict__ qkv, bf16* __restrict__ out,
+                                             float* __restrict__ lse, int T, int H, int b, int h,
+                                             int qt, int wave, float c_log2, unsigned int k_lds,
+                                             unsigned int v_lds) {
+    const int C = H * HEAD_DIM;
+    const long long rs = 3LL * C;
+    const int q0 = qt * FWD_BM;
+    const int qw = q0 + wave * 32;
+    const int kend = min(q0 + FWD_BM, T);
+    const int n_kt = (kend + FWD_BN - 1) / FWD_BN;
+    const int j_last = min((qw + 31) / FWD_BN, n_kt - 1);
+    const int nq = T - qw;  // queries of this wave inside the sequence (may be <= 0)
+    const int bh = b * H + h;
+
+    const unsigned long long k_at =
+        (unsigned long long)(uintptr_t)(qkv + (long long)b * T * rs + C + h * HEAD_DIM);
+    const unsigned long long k_left = (unsigned long long)T * rs * 2;
+    const unsigned long long q_row =
+        (unsigned long long)(uintptr_t)(qkv + ((long long)b * T + qw) * rs + h * HEAD_DIM);
+    const unsigned long long o_row =
+        (unsigned long long)(uintptr_t)(out + ((long long)b * T + qw) * C + h * HEAD_DIM);
+    const unsigned long long l_row = (unsigned long long)(uintptr_t)(lse + (long long)bh * T + qw);
+
+    asm volatile(CATTN_FWD_ASM_BODY
+                 :
+                 : [klds] "s"(k_lds), [vlds] "s"(v_lds),
+                   [kldw] "s"(k_lds + 2048u * wave), [vldw] "s"(v_lds + 2048u * wave),
+                   [wave16] "s"(16 * wave), [rs2] "s"((unsigned int)(rs * 2)),
+                   [c2] "s"((unsigned int)(C * 2)), [voffs] "s"((unsigned int)(C * 2)),
+                   [tbytes] "s"((unsigned int)(FWD_BN * rs * 2)),
+                   [kat_lo] "s"((unsigned int)k_at), [kat_hi] "s"((unsigned int)(k_at >> 32)),
+                   [kleft_lo] "s"((unsigned int)k_left),
+                   [kleft_hi] "s"((unsigned int)(k_left >> 32)),
+                   [nkt] "s"(n_kt), [jlast] "s"(j_last), [nq] "s"(nq), [nlse] "s"(min(nq, 32)),
+                   [limb] "s"(qw - j_last * FWD_BN),
+                   [cbits] "s"(__builtin_bit_cast(unsigned int, c_log2)),
+                   [qbase] "s"(q_row), [obase] "s"(o_row), [lbase] "s"(l_row)
+                 : CATTN_FWD_ASM_CLOBBERS, "vcc", "m0", "scc", "exec", "memory");
+}
+
+// Workgroup -> (query tile, head), heaviest (last) query tiles first; when
+// the head count allows, the heads are split into 8 contiguous groups, one
+// per XCD, so that K/V of a head stay in one L2.
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_asm_kernel(
+    const bf16* __restrict__ qkv, bf16* __restrict__ out, float* __restrict__ lse,
+    int B, int T, int H, int n_qt, float c_log2) {
+    __shared__ FwdSmem sm;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int BH = B * H;
+    const int blk = blockIdx.x;
+    int qt, bh;
+    if ((BH & 7) == 0) {
+        const int per = BH >> 3, xcd = blk & 7, s = blk >> 3;
+        qt = n_qt - 1 - s / per;
+        bh = xcd * per + s % per;
+    } else {
+        qt = n_qt - 1 - blk / BH;
+        bh = blk % BH;
+    }
+    const int b = bh / H, h = bh - b * H;
+    fwd_asm_item(qkv, out, lse, T, H, b, h, qt, wave, c_log2, atile_addr(sm.k[0]),
+                 atile_addr(sm.v[0]));
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const void* qkv, void* out, float* lse, int B, int T, int H,
@@ -284,7 +362,11 @@ hipError_t launch_attn_fwd_bf16(const void* qkv, void* out, float* lse, int B, i
     const int n_qt = (T + FWD_BM - 1) / FWD_BM;
     const long long blocks = (long long)B * H * n_qt;
     const float c_log2 = LOG2E / 8.0f;  // scale = 1/sqrt(64)
+#ifdef CATTN_FWD_COMPILED
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+#else
+    hipLaunchKernelGGL(attn_fwd_bf16_asm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+#endif
                        static_cast<const bf16*>(qkv), static_cast<bf16*>(out), lse, B, T, H,
                        n_qt, c_log2);
     return hipGetLastError();
