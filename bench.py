@@ -554,7 +554,17 @@ def measure_peaks(stream, dev):
     flops = binding.attn_peak_mfma_flops(n_wg, iters)
     out = torch.empty(256 * n_wg, dtype=torch.float32, device=dev)
     ticks = torch.empty(2 * n_wg, dtype=torch.int64, device=dev)
-    binding.attn_peak_mfma(out, ticks, n_wg, iters, stream)
+    # Sustained means after the clock has settled: the first milliseconds of
+    # load after idle run at a lower clock (about 1.3 GHz within 3 ms against
+    # about 1.9 GHz after 0.2 s under the attention kernels), so the probe
+    # repeats for 0.2 s before the calls it times. This also puts the timed
+    # steps, which follow, on a settled clock.
+    t_end = time.time() + 0.2
+    while True:
+        binding.attn_peak_mfma(out, ticks, n_wg, iters, stream)
+        torch.cuda.synchronize()
+        if time.time() >= t_end:
+            break
     rates = []
     for _ in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -386,3 +386,17 @@ def test_peak_probe_validation(L):
     assert L.attn_peak_read(Q + 4, 64, O, None) == -5
     assert L.attn_peak_read(Q, 64, O + 2, None) == -5
     assert L.attn_peak_read(Q, 1 << 20, Q + 64, None) == -6     # out inside src
+
+
+def test_documented_status_codes_and_workspace_formula(L):
+    """The numbering and the backward workspace size that the header and the
+    design notes document (boundary reading b1)."""
+    codes = {0: "ATTN_OK", -1: "ATTN_ERR_NULL_PTR", -2: "ATTN_ERR_BAD_SHAPE",
+             -3: "ATTN_ERR_UNSUPPORTED", -4: "ATTN_ERR_TOO_LARGE", -5: "ATTN_ERR_MISALIGNED",
+             -6: "ATTN_ERR_ALIAS", -7: "ATTN_ERR_HIP"}
+    header = open(os.path.join(ROOT, "include", "causal_attn.h")).read()
+    for code, name in codes.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", header), name
+        assert L.attn_status_string(code).decode() == name
+    for B, T, H in [(1, 1, 1), (16, 1024, 12), (3, 700, 5), (2, 64, 2), (4, 2049, 25)]:
+        assert L.attn_bwd_workspace_floats(B, T, H) == 10 * B * H * ((T + 63) // 64 * 64)
