@@ -407,6 +407,68 @@ __global__ __launch_bounds__(256, CATTN_DKDV_WAVES_PER_SIMD) void attn_bwd_dkdv_
     }
 }
 
+// The kernel the library launches for dK/dV: the same work as above with the
+// wave's whole program scheduled by hand (attn_dkdv_asm.inc, written by
+// gen_attn_dkdv_asm.py). The program pipelines 32-query halves: while the
+// VALU forms P and dS of one half, the matrix cores take dV/dK of the half
+// before it and S/dP of the half after it, each LDS operand read a few MFMAs
+// ahead. C++ maps the workgroup to (key tile, head) as above and hands the
+// program wave-uniform scalars.
+#include "attn_dkdv_asm.inc"
+
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_asm_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ ws,
+    bf16* __restrict__ dqkv, int B, int T, int Tp, int H, int n_kt, float c_log2, float scale) {
+    __shared__ DkdvSmem sm;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int BH = B * H;
+    const int blk = blockIdx.x;
+    int kt, bh;
+    if ((BH & 7) == 0) {
+        const int per = BH >> 3, xcd = blk & 7, s = blk >> 3;
+        kt = s / per;
+        bh = xcd * per + s % per;
+    } else {
+        kt = blk / BH;
+        bh = blk % BH;
+    }
+    const int b = bh / H, h = bh - b * H;
+    const int C = H * HEAD_DIM;
+    const long long rs = 3LL * C;
+    const int k0 = kt * KV_BN;
+    const int kw = k0 + wave * 32;
+    const int qt_begin = k0 / KV_BM;
+    const int n_it = (T + KV_BM - 1) / KV_BM - qt_begin;
+    const int q0 = qt_begin * KV_BM;
+    typedef unsigned long long u64;
+    const u64 q_at = (u64)(uintptr_t)(qkv + ((long long)b * T + q0) * rs + h * HEAD_DIM);
+    const u64 q_left = (u64)(T - q0) * (u64)rs * 2;
+    const u64 g_at = (u64)(uintptr_t)(dout + ((long long)b * T + q0) * C + h * HEAD_DIM);
+    const u64 g_left = (u64)(T - q0) * (u64)C * 2;
+    const u64 t_at = (u64)(uintptr_t)(reinterpret_cast<const char*>(ws + 2LL * BH * Tp) +
+                                      ((long long)bh * Tp + q0) * 32 + wave * 1024);
+    const u64 k_row = (u64)(uintptr_t)(qkv + ((long long)b * T + kw) * rs + C + h * HEAD_DIM);
+    const u64 dk_row = (u64)(uintptr_t)(dqkv + ((long long)b * T + kw) * rs + C + h * HEAD_DIM);
+    const unsigned int q_lds = atile_addr(sm.q[0]);
+    asm volatile(CATTN_DKDV_ASM_BODY
+                 :
+                 : [qlds] "s"(q_lds), [qldw] "s"(q_lds + 2048u * wave),
+                   [tldw] "s"(q_lds + 1024u * wave), [wave] "s"(wave), [wave16] "s"(16 * wave),
+                   [rs2] "s"((unsigned int)(rs * 2)), [c2] "s"((unsigned int)(C * 2)),
+                   [qtb] "s"((unsigned int)(KV_BM * rs * 2)), [gtb] "s"((unsigned int)(KV_BM * C * 2)),
+                   [qat_lo] "s"((unsigned int)q_at), [qat_hi] "s"((unsigned int)(q_at >> 32)),
+                   [qleft_lo] "s"((unsigned int)q_left), [qleft_hi] "s"((unsigned int)(q_left >> 32)),
+                   [gat_lo] "s"((unsigned int)g_at), [gat_hi] "s"((unsigned int)(g_at >> 32)),
+                   [gleft_lo] "s"((unsigned int)g_left), [gleft_hi] "s"((unsigned int)(g_left >> 32)),
+                   [tat_lo] "s"((unsigned int)t_at), [tat_hi] "s"((unsigned int)(t_at >> 32)),
+                   [nit] "s"(n_it), [nk] "s"(T - kw), [lim0] "s"(32 * (wave & 1)),
+                   [cbits] "s"(__builtin_bit_cast(unsigned int, c_log2)),
+                   [sbits] "s"(__builtin_bit_cast(unsigned int, scale)),
+                   [kbase] "s"(k_row), [vbase] "s"(k_row + 2ull * C),
+                   [dkbase] "s"(dk_row), [dvbase] "s"(dk_row + 2ull * C)
+                 : CATTN_DKDV_ASM_CLOBBERS, "vcc", "m0", "scc", "exec", "memory");
+}
+
 // ---------------------------------------------------------------------------
 // dQ. One workgroup = 4 waves = 128 queries of one (batch, head); wave w owns
 // queries q0 + 32w .. +31 with Q, dO, LSE*log2 e and D of its query in
@@ -622,7 +684,11 @@ hipError_t launch_attn_bwd_dkdv_bf16(const void* qkv, const void* dout, const fl
                                      int B, int T, int H, hipStream_t stream) {
     const int n_kt = (T + KV_BN - 1) / KV_BN;
     const long long blocks = (long long)B * H * n_kt;
+#ifdef CATTN_DKDV_COMPILED
     hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+#else
+    hipLaunchKernelGGL(attn_bwd_dkdv_bf16_asm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+#endif
                        static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), ws,
                        static_cast<bf16*>(dqkv), B, T, bwd_padded_rows(T), H, n_kt,
                        LOG2E / 8.0f, 0.125f);

@@ -87,7 +87,7 @@ class Prog:
                 if r in self.mfma_w:
                     need = max(need, self.mfma_w[r] + MFMA_RESULT_WAIT - self.idx)
         else:
-            for r in rd:
+            for r in list(rd) + list(wr):
                 if r in self.valu_w:
                     need = max(need, self.valu_w[r] + VALU_TO_MFMA_WAIT - self.idx)
         if kind == "valu" and not text.startswith(TRANS_OPS):
@@ -135,11 +135,13 @@ class Prog:
                 mine[r] = max(mine.get(r, pos + shift), pos + shift)
         assert self.lds == snap[3], "LDS queues differ at a join"
 
-    def reset(self, recent=()):
+    def reset(self, recent=(), recent_valu=None):
         """Block start with predecessors the tracker did not follow: the
-        registers in `recent` may have been written by MFMA or VALU just now."""
+        registers in `recent` may have been written by MFMA or VALU just now
+        (by VALU only for `recent_valu`, when given)."""
         self.mfma_w = {r: self.idx for r in recent}
-        self.valu_w = {r: self.idx for r in recent}
+        self.valu_w = {r: self.idx for r in (recent if recent_valu is None else
+                                              list(recent) + list(recent_valu))}
         self.trans_w = {}
         assert not self.lds, "LDS operations outstanding at a block start"
 
