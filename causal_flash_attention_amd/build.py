@@ -44,7 +44,7 @@ def hipcc() -> str:
 
 # Generators of hand-scheduled kernel programs: each writes an include next
 # to itself (committed, so that the sources build as they stand).
-GENERATORS = ["gen_attn_fwd_asm.py", "gen_attn_dkdv_asm.py"]
+GENERATORS = ["gen_attn_fwd_asm.py", "gen_attn_dkdv_asm.py", "gen_attn_dq_asm.py"]
 
 
 def generate() -> None:

@@ -663,6 +663,84 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     }
 }
 
+// The kernel the library launches for dQ with the preprocess: the wave's
+// whole program scheduled by hand (attn_dq_asm.inc, written by
+// gen_attn_dq_asm.py). It forms D and LSE * log2 e of its queries (the same
+// fmaf chain as the preprocess kernel, so the workspace matches it bit for
+// bit), stores the workspace rows while the tile loop runs, and pipelines
+// 32-key halves as the dK/dV program does: the scores and dP of one half and
+// dQ of another on MFMA while P and dS of the half between run on the VALU.
+#include "attn_dq_asm.inc"
+
+__global__ __launch_bounds__(256, 3) void attn_bwd_dq_pre_bf16_asm_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const bf16* __restrict__ out,
+    const float* __restrict__ lse, float* __restrict__ ws, bf16* __restrict__ dqkv, int B, int T,
+    int Tp, int H, int n_qt, float c_log2, float scale) {
+    __shared__ DqSmem sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int BH = B * H;
+    const int blk = blockIdx.x;
+    int qt, bh;
+    if ((BH & 7) == 0) {
+        const int per = BH >> 3, xcd = blk & 7, s = blk >> 3;
+        qt = n_qt - 1 - s / per;
+        bh = xcd * per + s % per;
+    } else {
+        qt = n_qt - 1 - blk / BH;
+        bh = blk % BH;
+    }
+    const int b = bh / H, h = bh - b * H;
+    const int C = H * HEAD_DIM;
+    const long long rs = 3LL * C;
+    const int q0 = qt * DQ_BM;
+    const int qw = q0 + wave * 32;
+    const int my_q = qw + l32;
+    const bool q_ok = my_q < T;
+
+    const int kend = min(q0 + DQ_BM, T);
+    const int n_kt = (kend + DQ_BN - 1) / DQ_BN;
+    const int k1 = min(qw / 32, 2 * n_kt - 1);  // this wave's last (diagonal) half
+    typedef unsigned long long u64;
+    const u64 k_at = (u64)(uintptr_t)(qkv + (long long)b * T * rs + C + h * HEAD_DIM);
+    const u64 k_left = (u64)T * (u64)rs * 2;
+    const u64 q_row = (u64)(uintptr_t)(qkv + ((long long)b * T + qw) * rs + h * HEAD_DIM);
+    const u64 g_row = (u64)(uintptr_t)(dout + ((long long)b * T + qw) * C + h * HEAD_DIM);
+    const u64 dq_row = (u64)(uintptr_t)(dqkv + ((long long)b * T + qw) * rs + h * HEAD_DIM);
+    const u64 o_row = (u64)(uintptr_t)(out + ((long long)b * T + qw) * C + h * HEAD_DIM);
+    const u64 l_row = (u64)(uintptr_t)(lse + (long long)bh * T + qw);
+    // this wave's workspace rows: D, LSE log2 e, and the 32-byte term rows
+    const long long r0 = (long long)bh * Tp + qw;
+    const u64 wsd = (u64)(uintptr_t)(ws + r0);
+    const u64 wsl = (u64)(uintptr_t)(ws + (long long)BH * Tp + r0);
+    const u64 wst = (u64)(uintptr_t)(reinterpret_cast<const char*>(ws + 2LL * BH * Tp) + r0 * 32);
+    const unsigned int k_lds = atile_addr(sm.k[0]);
+    asm volatile(CATTN_DQ_ASM_BODY
+                 :
+                 : [klds] "s"(k_lds), [kldw] "s"(k_lds + 2048u * wave), [wave16] "s"(16 * wave),
+                   [rs2] "s"((unsigned int)(rs * 2)), [c2] "s"((unsigned int)(C * 2)),
+                   [voffs] "s"((unsigned int)(C * 2)),
+                   [tbytes] "s"((unsigned int)(DQ_BN * rs * 2)),
+                   [kat_lo] "s"((unsigned int)k_at), [kat_hi] "s"((unsigned int)(k_at >> 32)),
+                   [kleft_lo] "s"((unsigned int)k_left), [kleft_hi] "s"((unsigned int)(k_left >> 32)),
+                   [nkt] "s"(n_kt), [k1] "s"(k1), [limb] "s"(qw - 32 * k1), [nq] "s"(T - qw),
+                   [cbits] "s"(__builtin_bit_cast(unsigned int, c_log2)),
+                   [sbits] "s"(__builtin_bit_cast(unsigned int, scale)),
+                   [qbase] "s"(q_row), [gbase] "s"(g_row), [dqbase] "s"(dq_row),
+                   [obase] "s"(o_row),
+                   [lbase_lo] "s"(__builtin_amdgcn_readfirstlane((unsigned int)l_row)),
+                   [lbase_hi] "s"(__builtin_amdgcn_readfirstlane((unsigned int)(l_row >> 32))),
+                   [wsd_lo] "s"(__builtin_amdgcn_readfirstlane((unsigned int)wsd)),
+                   [wsd_hi] "s"(__builtin_amdgcn_readfirstlane((unsigned int)(wsd >> 32))),
+                   [wsl_lo] "s"(__builtin_amdgcn_readfirstlane((unsigned int)wsl)),
+                   [wsl_hi] "s"(__builtin_amdgcn_readfirstlane((unsigned int)(wsl >> 32))),
+                   [wst_lo] "s"(__builtin_amdgcn_readfirstlane((unsigned int)wst)),
+                   [wst_hi] "s"(__builtin_amdgcn_readfirstlane((unsigned int)(wst >> 32))),
+                   [nw] "s"(min(32, Tp - qw))
+                 : CATTN_DQ_ASM_CLOBBERS, "vcc", "m0", "scc", "exec", "memory");
+}
+
 }  // namespace
 
 int bwd_padded_rows(int T) { return (T + ROW_PAD - 1) / ROW_PAD * ROW_PAD; }
@@ -711,7 +789,12 @@ hipError_t launch_attn_bwd_dq_pre_bf16(const void* qkv, const void* dout, const 
                                        int H, hipStream_t stream) {
     const int n_qt = (T + DQ_BM - 1) / DQ_BM;
     const long long blocks = (long long)B * H * n_qt;
+#ifdef CATTN_DQ_COMPILED
     hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+#else
+    hipLaunchKernelGGL(attn_bwd_dq_pre_bf16_asm_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       stream,
+#endif
                        static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout),
                        static_cast<const bf16*>(out), lse, ws, static_cast<bf16*>(dqkv), B, T,
                        bwd_padded_rows(T), H, n_qt, LOG2E / 8.0f, 0.125f);

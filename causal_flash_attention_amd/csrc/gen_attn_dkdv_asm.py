@@ -216,6 +216,66 @@ def phase2_ops(buf, mask):
 RING = 4
 
 
+def schedule(p, mfmas, reads, valu, cvts, n3, ring=RING):
+    """Emit MFMAs in order with their operand reads a few MFMAs ahead (two
+    register rings of RING operands, row and transposed) and the VALU queue
+    spread between them; `cvts` (which overwrite operands of the first n3
+    MFMAs) only after the n3-th MFMA has issued."""
+    pending = list(reads)
+    issued_tags = set()
+    ring_use = {"row": [], "tr": []}
+
+    def ring_of(rd):
+        return {"tr": "tr", "row": "row"}.get(rd.tag[0])
+
+    def can_issue(rd):
+        r = ring_of(rd)
+        return r is None or len(ring_use[r]) < ring
+
+    def issue_reads(limit):
+        n = 0
+        while pending and n < limit and can_issue(pending[0]):
+            rd = pending.pop(0)
+            for text, rr, ww in rd.ops:
+                p.lds_op(text, rd.tag, rr, ww)
+            which = ring_of(rd)
+            if which is not None:
+                ring_use[which].append(rd.tag)
+            issued_tags.add(rd.tag)
+            n += 1
+
+    issue_reads(ring + 1)
+    n_mf = len(mfmas)
+    queue = [(op, False) for op in valu] + [(op, True) for op in cvts]
+    per = [0] * max(n_mf, 1)
+    for i in range(len(queue)):
+        per[min(i * n_mf // len(queue), n_mf - 1)] += 1
+    qi = 0
+    carry = 0
+    for k, (dst, a, b, c, tag) in enumerate(mfmas):
+        if tag not in issued_tags:
+            issue_reads(len(pending))
+        assert tag in issued_tags, tag
+        p.wait_lds(tag)
+        p.mfma(dst, a, b, c)
+        for use in ring_use.values():
+            if tag in use:
+                use.remove(tag)
+        issue_reads(2)
+        carry += per[k]
+        while carry > 0 and qi < len(queue):
+            op, is_cvt = queue[qi]
+            if is_cvt and k < n3 - 1:
+                break
+            p.valu(*op)
+            qi += 1
+            carry -= 1
+    while qi < len(queue):
+        p.valu(*queue[qi][0])
+        qi += 1
+    p.wait_lds_all()
+
+
 def slot(p, ph3, ph1, ph2):
     """ph3 = (stage, qb) or None; ph1 = (stage, qb, buf) or None;
     ph2 = (buf, mask) or None."""
@@ -232,64 +292,7 @@ def slot(p, ph3, ph1, ph2):
     valu, cvts = phase2_ops(*ph2) if ph2 is not None else ([], [])
     if ph2 is not None and ph2[1] is not None:
         p.valu(f"v_mov_b32 v{T0}, 0xff800000", [], [T0])
-    # reads in MFMA order; each ring (row, transposed) holds RING operands
-    pending = list(reads)
-    issued_tags = set()
-    ring_use = {"row": [], "tr": []}
-
-    def ring_of(rd):
-        return "tr" if rd.tag[0] == "tr" else ("row" if rd.tag[0] == "row" else None)
-
-    def can_issue(rd):
-        ring = ring_of(rd)
-        if ring is None:
-            return True
-        return len(ring_use[ring]) < RING
-
-    def issue_reads(limit):
-        n = 0
-        while pending and n < limit and can_issue(pending[0]):
-            rd = pending.pop(0)
-            for text, rr, ww in rd.ops:
-                p.lds_op(text, rd.tag, rr, ww)
-            ring = ring_of(rd)
-            if ring is not None:
-                ring_use[ring].append(rd.tag)
-            issued_tags.add(rd.tag)
-            n += 1
-
-    issue_reads(RING + 1)
-    n_mf = len(mfmas)
-    # Phase 2 in one queue, conversions last: they overwrite the B operands
-    # of phase 3, so none is emitted before the last phase-3 MFMA has issued.
-    queue = [(op, False) for op in valu] + [(op, True) for op in cvts]
-    per = [0] * max(n_mf, 1)
-    for i in range(len(queue)):
-        per[min(i * n_mf // len(queue), n_mf - 1)] += 1
-    qi = 0
-    carry = 0
-    for k, (dst, a, b, c, tag) in enumerate(mfmas):
-        if tag not in issued_tags:
-            issue_reads(len(pending))
-        assert tag in issued_tags, tag
-        p.wait_lds(tag)
-        p.mfma(dst, a, b, c)
-        for ring in ring_use.values():
-            if tag in ring:
-                ring.remove(tag)
-        issue_reads(2)
-        carry += per[k]
-        while carry > 0 and qi < len(queue):
-            op, is_cvt = queue[qi]
-            if is_cvt and k < n3 - 1:
-                break
-            p.valu(*op)
-            qi += 1
-            carry -= 1
-    while qi < len(queue):
-        p.valu(*queue[qi][0])
-        qi += 1
-    p.wait_lds_all()
+    schedule(p, mfmas, reads, valu, cvts, n3)
 
 
 # ---------------------------------------------------------------------------

@@ -17,6 +17,7 @@ CSRC = os.path.join(ROOT, "causal_flash_attention_amd", "csrc")
 sys.path.insert(0, CSRC)
 
 import gen_attn_dkdv_asm as gen_dkdv  # noqa: E402
+import gen_attn_dq_asm as gen_dq  # noqa: E402
 import gen_attn_fwd_asm as gen  # noqa: E402
 from asm_flow import Flow  # noqa: E402
 
@@ -26,7 +27,8 @@ def swz(r):
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
 
 
-@pytest.mark.parametrize("script", ["gen_attn_fwd_asm.py", "gen_attn_dkdv_asm.py"])
+@pytest.mark.parametrize("script", ["gen_attn_fwd_asm.py", "gen_attn_dkdv_asm.py",
+                                    "gen_attn_dq_asm.py"])
 def test_include_is_current(script):
     res = subprocess.run([sys.executable, os.path.join(CSRC, script), "--check"],
                          capture_output=True, text=True)
@@ -76,6 +78,10 @@ def test_program_hazard_distances_fwd():
 
 def test_program_hazard_distances_dkdv():
     _check_hazard_distances(gen_dkdv.program())
+
+
+def test_program_hazard_distances_dq():
+    _check_hazard_distances(gen_dq.program())
 
 
 def _check_hazard_distances(lines):
@@ -200,3 +206,41 @@ def test_dkdv_reads_between_publish_and_refill(n_it):
                 cands = [t for t in range(n_it + 3)
                          if t % 3 == st and max(1, t + 1) <= nb < t + 3]
                 assert len(cands) == 1, (w, nb, ln)
+
+
+@pytest.mark.parametrize("n_kt", [1, 2, 3, 4, 7, 11])
+def test_dq_schedule(n_kt):
+    """Per wave, for every position of its diagonal half k1: n_kt + 1
+    barriers and 4 tile-load instructions per tile; S/dP and dQ of halves
+    0 .. k1 each once, in order, from the stage tile k // 2 occupies; one
+    masked half; every LDS read between its tile's publication and refill."""
+    lines = gen_dq.program()
+    for k1 in range(2 * n_kt):
+        f = Flow(lines, {"nkt": n_kt, "k1": k1})
+        bars, loads = f.run()
+        assert bars == n_kt + 1 and len(loads) == 4 * n_kt
+        p1, p3, masks, nb = [], [], 0, 0
+        for ln in f.trace:
+            if ln == "s_barrier":
+                nb += 1
+                continue
+            m = re.match(rf"ds_read_b128 v\[\d+:\d+\], v{gen_dq.ROFF} offset:(\d+)", ln)
+            if m and int(m.group(1)) < gen_dq.V_OFF:
+                o = int(m.group(1))
+                p1.append((o // gen_dq.STAGE, (o % gen_dq.STAGE) // 4096))
+            m = re.match(rf"ds_read_b64_tr_b16 v\[\d+:\d+\], v{gen_dq.TROFF} offset:(\d+)", ln)
+            if m:
+                o = int(m.group(1))
+                st, kc = o // gen_dq.STAGE, (o % gen_dq.STAGE) // 2048
+                if kc % 2 == 0:
+                    p3.append((st, kc // 2))
+            if re.match(rf"v_cmp_gt_i32_e64 \S+, 0, v{gen_dq.LIM}", ln):
+                masks += 1
+            if ln.startswith("ds_read"):
+                o = int(re.search(r"offset:(\d+)", ln).group(1))
+                st = (o % gen_dq.V_OFF) // gen_dq.STAGE
+                cands = [t for t in range(n_kt + 3)
+                         if t % 3 == st and max(1, t + 1) <= nb < t + 3]
+                assert len(cands) == 1, (k1, nb, ln)
+        want = [((k // 2) % 3, k % 2) for k in range(k1 + 1)]
+        assert p1 == want and p3 == want and masks == 1
