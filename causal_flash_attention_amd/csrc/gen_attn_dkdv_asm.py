@@ -41,7 +41,7 @@ import sys
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
-from gen_attn_fwd_asm import Prog, emit_lane_setup, vt  # noqa: E402
+from gen_attn_fwd_asm import Prog, emit_lane_setup, lane_halves, vt  # noqa: E402
 
 KREG, VREG, SD0, SD1, PDS = 0, 16, 32, 64, 96
 ROW, TERMS, TR = 112, 128, 132
@@ -304,17 +304,9 @@ def program():
     lane = T1
     p.valu(f"v_mbcnt_lo_u32_b32 v{lane}, -1, 0", [], [lane])
     p.valu(f"v_mbcnt_hi_u32_b32 v{lane}, -1, v{lane}", [lane], [lane])
-    # scratch for the lane arithmetic: the S/dP buffers (free until phase 1)
-    regs = {f"koff{kk}": ROFF + kk for kk in range(4)}
-    regs.update({f"voff{db}{h}": TROFF + 2 * db + h for db in range(2) for h in range(2)})
-    loc = emit_lane_setup(p, regs, lane)
-    l32, hf = loc["l32"], loc["hf"]
-    for r in list(range(ROFF, ROFF + 4)) + list(range(TROFF, TROFF + 4)):
-        p.valu(f"v_add_u32 v{r}, %[qlds], v{r}", [r], [r])
-    # terms read offset: hf 512 + l32 16 (+ the LDS base)
-    p.valu(f"v_lshlrev_b32 v{TOFF}, 4, v{l32}", [l32], [TOFF])
-    p.valu(f"v_lshl_add_u32 v{TOFF}, v{hf}, 9, v{TOFF}", [hf, TOFF], [TOFF])
-    p.valu(f"v_add_u32 v{TOFF}, %[qlds], v{TOFF}", [TOFF], [TOFF])
+    # l32 and hf first, so that the loads go out before the rest of the lane
+    # arithmetic (which recomputes them in place)
+    l32, hf = lane_halves(p, lane)
     # tile-load offsets: row tr = 16 wave + 8 i + lane/8, chunk (lane & 7) ^ swz(tr)
     t_l3, t_tr, t_sw, t_x, t_ko = 88, 89, 90, 91, 92
     p.valu(f"v_lshrrev_b32 v{t_l3}, 3, v{lane}", [lane], [t_l3])
@@ -334,24 +326,6 @@ def program():
         p.valu(f"v_mul_lo_u32 v{LDG + i}, v{t_tr}, %[c2]", [t_tr], [LDG + i])
         p.valu(f"v_add_u32 v{LDG + i}, v{LDG + i}, v{t_x}", [LDG + i, t_x], [LDG + i])
     p.valu(f"v_lshlrev_b32 v{LDT}, 4, v{lane}", [lane], [LDT])
-    # the terms k-step's B operands: -1 on the first three k of lane half 0
-    # (S) or 1 (dP)
-    p.valu(f"v_cmp_eq_u32 vcc, 0, v{hf}", [hf], [])
-    for base, hf0 in ((BS, True), (BD, False)):
-        for r, word in enumerate((0xBF80BF80, 0x0000BF80, 0, 0)):
-            if word == 0:
-                p.valu(f"v_mov_b32 v{base + r}, 0", [], [base + r])
-            elif hf0:
-                p.valu(f"v_mov_b32 v{T0}, {word:#x}", [], [T0])
-                p.valu(f"v_cndmask_b32_e64 v{base + r}, 0, v{T0}, vcc", [T0], [base + r])
-            else:
-                p.valu(f"v_mov_b32 v{T0}, {word:#x}", [], [T0])
-                p.valu(f"v_cndmask_b32_e64 v{base + r}, v{T0}, 0, vcc", [T0], [base + r])
-    # mask limit of the wave's first tile: l32 - 4 hf + 32 (wave & 1)
-    p.valu(f"v_lshlrev_b32 v{LIM}, 2, v{hf}", [hf], [LIM])
-    p.valu(f"v_sub_u32 v{LIM}, v{l32}, v{LIM}", [l32, LIM], [LIM])
-    p.valu(f"v_add_u32 v{LIM}, %[lim0], v{LIM}", [LIM], [LIM])
-    p.valu(f"v_mov_b32 v{CREG}, %[cbits]", [], [CREG])
     # K and V row offset: l32 * row stride + 16 hf
     p.valu(f"v_mul_lo_u32 v{t_ko}, v{l32}, %[rs2]", [l32], [t_ko])
     p.valu(f"v_lshl_add_u32 v{t_ko}, v{hf}, 4, v{t_ko}", [hf, t_ko], [t_ko])
@@ -375,6 +349,36 @@ def program():
         p.emit(f"global_load_dwordx4 {vt(VREG + 4 * kk, 4)}, v{t_ko}, %[vbase] offset:{32 * kk}",
                "vmem", [t_ko], list(range(VREG + 4 * kk, VREG + 4 * kk + 4)))
     p.emit(f"s_mov_b64 exec, s[{SEXEC}:{SEXEC + 1}]")
+    # the rest of the lane arithmetic while the loads are in flight (scratch:
+    # the S/dP buffers, free until phase 1)
+    regs = {f"koff{kk}": ROFF + kk for kk in range(4)}
+    regs.update({f"voff{db}{h}": TROFF + 2 * db + h for db in range(2) for h in range(2)})
+    loc = emit_lane_setup(p, regs, lane)
+    assert (loc["l32"], loc["hf"]) == (l32, hf)
+    for r in list(range(ROFF, ROFF + 4)) + list(range(TROFF, TROFF + 4)):
+        p.valu(f"v_add_u32 v{r}, %[qlds], v{r}", [r], [r])
+    # terms read offset: hf 512 + l32 16 (+ the LDS base)
+    p.valu(f"v_lshlrev_b32 v{TOFF}, 4, v{l32}", [l32], [TOFF])
+    p.valu(f"v_lshl_add_u32 v{TOFF}, v{hf}, 9, v{TOFF}", [hf, TOFF], [TOFF])
+    p.valu(f"v_add_u32 v{TOFF}, %[qlds], v{TOFF}", [TOFF], [TOFF])
+    # the terms k-step's B operands: -1 on the first three k of lane half 0
+    # (S) or 1 (dP)
+    p.valu(f"v_cmp_eq_u32 vcc, 0, v{hf}", [hf], [])
+    for base, hf0 in ((BS, True), (BD, False)):
+        for r, word in enumerate((0xBF80BF80, 0x0000BF80, 0, 0)):
+            if word == 0:
+                p.valu(f"v_mov_b32 v{base + r}, 0", [], [base + r])
+            elif hf0:
+                p.valu(f"v_mov_b32 v{T0}, {word:#x}", [], [T0])
+                p.valu(f"v_cndmask_b32_e64 v{base + r}, 0, v{T0}, vcc", [T0], [base + r])
+            else:
+                p.valu(f"v_mov_b32 v{T0}, {word:#x}", [], [T0])
+                p.valu(f"v_cndmask_b32_e64 v{base + r}, v{T0}, 0, vcc", [T0], [base + r])
+    # mask limit of the wave's first tile: l32 - 4 hf + 32 (wave & 1)
+    p.valu(f"v_lshlrev_b32 v{LIM}, 2, v{hf}", [hf], [LIM])
+    p.valu(f"v_sub_u32 v{LIM}, v{l32}, v{LIM}", [l32, LIM], [LIM])
+    p.valu(f"v_add_u32 v{LIM}, %[lim0], v{LIM}", [LIM], [LIM])
+    p.valu(f"v_mov_b32 v{CREG}, %[cbits]", [], [CREG])
     for r in acc + list(range(PDS, PDS + 16)):
         p.valu(f"v_mov_b32 v{r}, 0", [], [r])
     p.emit("s_waitcnt vmcnt(0)")

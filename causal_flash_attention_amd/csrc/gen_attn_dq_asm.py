@@ -40,7 +40,7 @@ import sys
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
 from gen_attn_dkdv_asm import Read, schedule  # noqa: E402
-from gen_attn_fwd_asm import Prog, emit_lane_setup, vt  # noqa: E402
+from gen_attn_fwd_asm import Prog, emit_lane_setup, lane_halves, vt  # noqa: E402
 
 QREG, GREG, SD0, SD1, DS = 0, 16, 32, 64, 96
 ROW, TR = 104, 112
@@ -271,12 +271,9 @@ def program():
     lane = LANE
     p.valu(f"v_mbcnt_lo_u32_b32 v{lane}, -1, 0", [], [lane])
     p.valu(f"v_mbcnt_hi_u32_b32 v{lane}, -1, v{lane}", [lane], [lane])
-    regs = {f"koff{kk}": ROFF + kk for kk in range(4)}
-    regs.update({f"voff{db}{h}": TROFF + 2 * db + h for db in range(2) for h in range(2)})
-    loc = emit_lane_setup(p, regs, lane)
-    l32, hf = loc["l32"], loc["hf"]
-    for r in list(range(ROFF, ROFF + 4)) + list(range(TROFF, TROFF + 4)):
-        p.valu(f"v_add_u32 v{r}, %[klds], v{r}", [r], [r])
+    # l32 and hf first, so that the loads go out before the rest of the lane
+    # arithmetic (which recomputes them in place)
+    l32, hf = lane_halves(p, lane)
     t_l3, t_tr, t_sw, t_x, t_qo, t_go = 88, 89, 90, 91, 92, 93
     p.valu(f"v_lshrrev_b32 v{t_l3}, 3, v{lane}", [lane], [t_l3])
     for i in range(2):
@@ -292,10 +289,6 @@ def program():
         p.valu(f"v_lshlrev_b32 v{t_x}, 4, v{t_x}", [t_x], [t_x])
         p.valu(f"v_mul_lo_u32 v{LDOFF + i}, v{t_tr}, %[rs2]", [t_tr], [LDOFF + i])
         p.valu(f"v_add_u32 v{LDOFF + i}, v{LDOFF + i}, v{t_x}", [LDOFF + i, t_x], [LDOFF + i])
-    # mask limit of the diagonal half: l32 - 4 hf + (qw - 32 k1)
-    p.valu(f"v_lshlrev_b32 v{LIM}, 2, v{hf}", [hf], [LIM])
-    p.valu(f"v_sub_u32 v{LIM}, v{l32}, v{LIM}", [l32, LIM], [LIM])
-    p.valu(f"v_add_u32 v{LIM}, %[limb], v{LIM}", [LIM], [LIM])
     p.valu(f"v_mul_lo_u32 v{t_qo}, v{l32}, %[rs2]", [l32], [t_qo])
     p.valu(f"v_lshl_add_u32 v{t_qo}, v{hf}, 4, v{t_qo}", [hf, t_qo], [t_qo])
     p.valu(f"v_mul_lo_u32 v{t_go}, v{l32}, %[c2]", [l32], [t_go])
@@ -324,7 +317,7 @@ def program():
                "vmem", [t_go], list(range(GREG + 4 * kk, GREG + 4 * kk + 4)))
     p.emit(f"s_mov_b64 exec, s[{SEXEC}:{SEXEC + 1}]")
     # O of this lane's query (zeros past the sequence) and its LSE
-    ob, t_lo = 64, 95
+    ob, t_lo = 76, 95      # clear of the lane arithmetic scratch (v48-74) while in flight
     for r in range(ob, ob + 16):
         p.valu(f"v_mov_b32 v{r}, 0", [], [r])
     p.valu(f"v_mov_b32 v{LSE2}, 0x7f800000", [], [LSE2])
@@ -337,6 +330,18 @@ def program():
                "vmem", [t_go], list(range(ob + 4 * kk, ob + 4 * kk + 4)))
     p.emit(f"global_load_dword v{LSE2}, v{t_lo}, s[{SLB}:{SLB + 1}]", "vmem", [t_lo], [LSE2])
     p.emit(f"s_mov_b64 exec, s[{SEXEC}:{SEXEC + 1}]")
+    # the rest of the lane arithmetic while the loads are in flight
+    regs = {f"koff{kk}": ROFF + kk for kk in range(4)}
+    regs.update({f"voff{db}{h}": TROFF + 2 * db + h for db in range(2) for h in range(2)})
+    loc = emit_lane_setup(p, regs, lane)
+    assert (loc["l32"], loc["hf"]) == (l32, hf)
+    for r in list(range(ROFF, ROFF + 4)) + list(range(TROFF, TROFF + 4)):
+        p.valu(f"v_add_u32 v{r}, %[klds], v{r}", [r], [r])
+    # mask limit of the diagonal half: l32 - 4 hf + (qw - 32 k1)
+    p.valu(f"v_lshlrev_b32 v{LIM}, 2, v{hf}", [hf], [LIM])
+    p.valu(f"v_sub_u32 v{LIM}, v{l32}, v{LIM}", [l32, LIM], [LIM])
+    p.valu(f"v_add_u32 v{LIM}, %[limb], v{LIM}", [LIM], [LIM])
+
     for r in acc + list(range(DS, DS + 8)):
         p.valu(f"v_mov_b32 v{r}, 0", [], [r])
     p.emit("s_waitcnt vmcnt(0)")

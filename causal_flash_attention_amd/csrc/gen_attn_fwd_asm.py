@@ -72,6 +72,7 @@ class Prog:
         self.valu_w = {}      # vgpr -> slot of the VALU/memory op that last wrote it
         self.trans_w = {}     # vgpr -> slot of the transcendental that last wrote it
         self.lds = []         # outstanding LDS operations (tags), oldest first
+        self.vmem_dst = set() # VGPRs a global load in flight will still write
 
     def _nop(self, n):
         while n > 0:
@@ -81,6 +82,11 @@ class Prog:
             n -= k
 
     def emit(self, text, kind="salu", rd=(), wr=()):
+        if text.startswith("s_waitcnt vmcnt(0)"):
+            self.vmem_dst = set()
+        touched = (set(rd) | set(wr)) & self.vmem_dst
+        if touched:
+            raise AssertionError(f"{text}: touches v{sorted(touched)} before their load lands")
         need = 0
         if kind != "mfma":
             for r in list(rd) + list(wr):
@@ -98,6 +104,8 @@ class Prog:
         self.lines.append(text)
         pos = self.idx
         self.idx += 1
+        if kind == "vmem" and wr:
+            self.vmem_dst |= set(wr)
         for r in wr:
             self.trans_w.pop(r, None)
             if kind == "mfma":
@@ -251,6 +259,15 @@ def eval_lane_setup(lane):
         else:
             raise ValueError(k)
     return env
+
+
+def lane_halves(p, lane_reg):
+    """l32 = lane & 31 and hf = lane >> 5 into the registers emit_lane_setup
+    gives them (the first two of its scratch)."""
+    l32, hf = SB, SB + 1
+    p.valu(f"v_and_b32 v{l32}, 31, v{lane_reg}", [lane_reg], [l32])
+    p.valu(f"v_lshrrev_b32 v{hf}, 5, v{lane_reg}", [lane_reg], [hf])
+    return l32, hf
 
 
 def emit_lane_setup(p, regmap, lane_reg):
@@ -505,14 +522,9 @@ def program():
     lane = 163
     p.valu(f"v_mbcnt_lo_u32_b32 v{lane}, -1, 0", [], [lane])
     p.valu(f"v_mbcnt_hi_u32_b32 v{lane}, -1, v{lane}", [lane], [lane])
-    regs = {f"koff{kk}": KOFF + kk for kk in range(4)}
-    regs.update({f"voff{db}{h}": VOFF + 2 * db + h for db in range(2) for h in range(2)})
-    loc = emit_lane_setup(p, regs, lane)
-    l32, hf = loc["l32"], loc["hf"]
-    for kk in range(4):
-        p.valu(f"v_add_u32 v{KOFF + kk}, %[klds], v{KOFF + kk}", [KOFF + kk], [KOFF + kk])
-    for k in range(4):
-        p.valu(f"v_add_u32 v{VOFF + k}, %[vlds], v{VOFF + k}", [VOFF + k], [VOFF + k])
+    # l32 and hf first (the lane arithmetic below recomputes them in place),
+    # so that the loads go out before the rest of the lane arithmetic
+    l32, hf = lane_halves(p, lane)
     # tile loads: row tr = 16 wave + 8 i + (lane >> 3), chunk (lane & 7) ^ swz(tr)
     t_lane3, t_tr, t_sw, t_x, t_qo = SB + 27, SB + 28, SB + 29, SB + 30, SB + 31
     p.valu(f"v_lshrrev_b32 v{t_lane3}, 3, v{lane}", [lane], [t_lane3])
@@ -555,6 +567,15 @@ def program():
         p.emit(f"global_load_dwordx4 {vt(Q + 4 * kk, 4)}, v{t_qo}, %[qbase] offset:{32 * kk}", "vmem",
                [t_qo], list(range(Q + 4 * kk, Q + 4 * kk + 4)))
     p.emit(f"s_mov_b64 exec, s[{SEXEC}:{SEXEC + 1}]")
+    # the rest of the lane arithmetic while the loads are in flight
+    regs = {f"koff{kk}": KOFF + kk for kk in range(4)}
+    regs.update({f"voff{db}{h}": VOFF + 2 * db + h for db in range(2) for h in range(2)})
+    loc = emit_lane_setup(p, regs, lane)
+    assert (loc["l32"], loc["hf"]) == (l32, hf)
+    for kk in range(4):
+        p.valu(f"v_add_u32 v{KOFF + kk}, %[klds], v{KOFF + kk}", [KOFF + kk], [KOFF + kk])
+    for k in range(4):
+        p.valu(f"v_add_u32 v{VOFF + k}, %[vlds], v{VOFF + k}", [VOFF + k], [VOFF + k])
     p.valu(f"v_xor_b32 v{BPERM}, 32, v{lane}", [lane], [BPERM])
     p.valu(f"v_lshlrev_b32 v{BPERM}, 2, v{BPERM}", [BPERM], [BPERM])
     p.valu(f"v_mov_b32 v{NINF}, 0xff800000", [], [NINF])
