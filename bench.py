@@ -124,9 +124,21 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def source_digest(path: str) -> str:
+# The generated programs the step's kernels run (their code is in these
+# includes, so a change to one changes the kernel).
+GENERATED = {"attn_fwd": ["attn_fwd_asm.inc"], "attn_bwd_dq_preprocess": ["attn_dq_asm.inc"],
+             "attn_bwd_dkdv": ["attn_dkdv_asm.inc"]}
+
+
+def kernel_digest(kernel: str) -> str:
+    src = (KERNELS.get(kernel) or EXTRA_TRAFFIC[kernel])[0]
+    return source_digest(os.path.join(CSRC, src),
+                         [os.path.join(CSRC, f) for f in GENERATED.get(kernel, [])])
+
+
+def source_digest(path: str, extra=()) -> str:
     h = hashlib.sha256()
-    for f in sorted({os.path.join(CSRC, "attn_common.h"), path}):
+    for f in sorted({os.path.join(CSRC, "attn_common.h"), path, *extra}):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -143,7 +155,7 @@ def traffic_from_profile(kernel: str, workload: str):
     m_val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     if not (m_src and m_val):
         return None
-    if m_src.group(1) != source_digest(os.path.join(CSRC, (KERNELS.get(kernel) or EXTRA_TRAFFIC[kernel])[0])):
+    if m_src.group(1) != kernel_digest(kernel):
         return None
     return float(m_val.group(1))
 
@@ -162,6 +174,8 @@ def _csv_rows(d: str, suffix: str):
 
 
 def _kernel_of(name: str):
+    if "attn_bwd_dq_pre_bf16_asm_kernel" in name:  # what attn_bwd launches for dQ
+        return "attn_bwd_dq_preprocess"
     if "attn_bwd_dq_bf16_kernel" in name:  # <true>: the fused form attn_bwd launches
         return "attn_bwd_dq_preprocess" if ("<true>" in name or "ILb1E" in name) else "attn_bwd_dq"
     m = re.search(r"gemm_bf16_kernel<(\d), (\d), (\d+), (true|false)>", name)
@@ -185,7 +199,9 @@ def _kernel_of(name: str):
                    ("peak_read", "peak_read_kernel")):
         if tag in name:
             return k
-    for k, tag in (("attn_fwd", "attn_fwd_bf16_kernel"), ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
+    for k, tag in (("attn_fwd", "attn_fwd_bf16_asm_kernel"), ("attn_fwd", "attn_fwd_bf16_kernel"),
+                   ("attn_bwd_preprocess", "attn_bwd_pre_bf16_kernel"),
+                   ("attn_bwd_dkdv", "attn_bwd_dkdv_bf16_asm_kernel"),
                    ("attn_bwd_dkdv", "attn_bwd_dkdv_bf16_kernel")):
         if tag in name:
             return k
@@ -348,7 +364,7 @@ def write_profiles(args, w) -> int:
             text = "\n".join([
                 f"# HBM traffic of {k} on workload {w.name}, from rocprofv3 counters",
                 f"# command: {cmd}",
-                f"source_sha256_16: {source_digest(os.path.join(CSRC, (KERNELS.get(k) or EXTRA_TRAFFIC[k])[0]))}",
+                f"source_sha256_16: {kernel_digest(k)}",
                 f"fetch_kib_per_dispatch: {fetch[k]:.1f}",
                 f"write_kib_per_dispatch: {write[k]:.1f}",
                 f"copy_calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE "

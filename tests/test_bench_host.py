@@ -137,7 +137,11 @@ def test_write_and_read_back_profiles(profiles):
     # A profile taken on other sources is not used.
     f = p / f"attn_bwd_dkdv_{HEADLINE.name}_hbm_traffic.txt"
     text = f.read_text()
-    digest = bench.source_digest(os.path.join(bench.CSRC, "attn_bwd_bf16.hip"))
+    # the digest covers the kernel's source file and its generated program
+    digest = bench.source_digest(os.path.join(bench.CSRC, "attn_bwd_bf16.hip"),
+                                 [os.path.join(bench.CSRC, "attn_dkdv_asm.inc")])
+    assert digest == bench.kernel_digest("attn_bwd_dkdv")
+    assert digest != bench.source_digest(os.path.join(bench.CSRC, "attn_bwd_bf16.hip"))
     assert f"source_sha256_16: {digest}" in text
     f.write_text(text.replace(digest, "0" * 16))
     assert bench.traffic_from_profile("attn_bwd_dkdv", HEADLINE.name) is None
