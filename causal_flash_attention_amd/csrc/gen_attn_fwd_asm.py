@@ -443,10 +443,103 @@ def max_tail(p, name):
     p.join(snap)
 
 
+# The rescale test. After the exponentials of a tile with the row's current
+# reference m, each lane sums its 32 P values: if no sum exceeds 2^8, no P
+# does, and the tile needs nothing more. Otherwise (rarely: a row's scores
+# grew past its reference) the program leaves the straight path for a block
+# that recomputes the tile's scores, takes the row max, moves m and rescales
+# l and O for the rows whose sums exceeded 2^8 (in either lane half), and
+# redoes the exponentials. Rows that did not trigger recompute bit-identical
+# values with their unchanged m and scale by exactly 1, so a row's arithmetic
+# never depends on the other rows of the wave.
+SUM_LIMIT = "0x43800000"   # 256.0
+REDO = []                   # out-of-line blocks, emitted after the epilogue
+
+
+def sums_into(p, cur, elems):
+    for e in elems:
+        t = T0 if e % 2 == 0 else T1
+        p.valu(f"v_add_f32 v{t}, v{t}, v{cur + e}", [t, cur + e], [t])
+
+
+def rescale_check(p, r, cur, kind):
+    """The test and its out-of-line block; returns with L updated."""
+    p.valu(f"v_add_f32 v{T0}, v{T0}, v{T1}", [T0, T1], [T0])
+    p.valu(f"v_cmp_lt_f32 vcc, {SUM_LIMIT}, v{T0}", [T0], [])
+    name = f"fwd_redo{kind}{r}"
+    snap = p.snapshot()
+    p.emit(f"s_cbranch_vccnz {name}_%=")
+    REDO.append((name, r, cur, kind, snap))
+    p.label(f"{name}_ret")
+    # the block's last writes before it branches back are VALU (its score
+    # MFMAs lie far behind); the LDS queue of the straight path is kept,
+    # which only over-counts after the block has drained it
+    for reg in (list(range(cur, cur + 32)) + list(range(ACC, ACC + 32)) +
+                list(range(P, P + 16)) + [M, L0, L1, T0, T1]):
+        p.valu_w[reg] = p.idx
+        p.trans_w.pop(reg, None)
+    p.valu(f"v_add_f32 v{L0}, v{L0}, v{T0}", [L0, T0], [L0])
+
+
+def redo_block(p, name, r, cur, kind, snap):
+    """Recompute the tile's scores (K of tile j is still in its stage), mask
+    them on the diagonal tile, move m for the rows that triggered, rescale,
+    and redo the exponentials, the sums and the P operands made before the
+    test. T0 holds the lane's sum on entry."""
+    st = r % 3
+    p.restore(snap)
+    p.label(name)
+    for f in range(8):
+        kk, kb = f // 2, f % 2
+        read_k(p, st, f)
+        p.wait_lds(("k", f))
+        p.mfma(cur + 16 * kb, KR + 4 * (f % 2), Q + 4 * kk, None if kk == 0 else cur + 16 * kb)
+    p.lds_op(f"ds_bpermute_b32 v{T1}, v{BPERM}, v{T0}", ("rb",), [BPERM, T0], [T1])
+    if kind == "final":
+        mask_scores(p, cur)
+    # rows to move: this lane's sum or its partner's exceeded the limit
+    flag = f"s[{SCMP}:{SCMP + 1}]"
+    p.valu(f"v_cmp_lt_f32 vcc, {SUM_LIMIT}, v{T0}", [T0], [])
+    p.emit(f"s_mov_b64 {flag}, vcc")
+    p.wait_lds(("rb",))
+    p.valu(f"v_cmp_lt_f32 vcc, {SUM_LIMIT}, v{T1}", [T1], [])
+    p.emit(f"s_or_b64 {flag}, {flag}, vcc")
+    for op in max_ops(cur):
+        emit_max_op(p, cur, op)
+    p.lds_op(f"ds_bpermute_b32 v{T0}, v{BPERM}, v{MX}", ("bperm",), [BPERM, MX], [T0])
+    p.wait_lds(("bperm",))
+    p.valu(f"v_max_f32 v{MX}, v{MX}, v{T0}", [MX, T0], [MX])
+    p.valu(f"v_mul_f32 v{MX}, v{MX}, v{CREG}", [MX, CREG], [MX])
+    # m_new = max(m, tile max) on the rows that triggered, m elsewhere
+    p.valu(f"v_max_f32 v{T0}, v{M}, v{MX}", [M, MX], [T0])
+    p.valu(f"v_cndmask_b32_e64 v{T1}, v{M}, v{T0}, {flag}", [M, T0], [T1])
+    p.valu(f"v_sub_f32 v{T0}, v{M}, v{T1}", [M, T1], [T0])
+    p.valu(f"v_exp_f32 v{T0}, v{T0}", [T0], [T0])
+    p.valu(f"v_cndmask_b32_e64 v{T0}, 1.0, v{T0}, {flag}", [T0], [T0])
+    p.valu(f"v_mul_f32 v{L0}, v{L0}, v{T0}", [L0, T0], [L0])
+    p.valu(f"v_mul_f32 v{L1}, v{L1}, v{T0}", [L1, T0], [L1])
+    for reg in range(ACC, ACC + 32):
+        p.valu(f"v_mul_f32 v{reg}, v{reg}, v{T0}", [reg, T0], [reg])
+    p.valu(f"v_mov_b32 v{M}, v{T1}", [T1], [M])
+    exps(p, cur, range(32))
+    p.valu(f"v_mov_b32 v{T0}, 0", [], [T0])
+    p.valu(f"v_mov_b32 v{T1}, 0", [], [T1])
+    sums_into(p, cur, range(32))
+    p.valu(f"v_add_f32 v{T0}, v{T0}, v{T1}", [T0, T1], [T0])
+    n_cvt = 4 if kind == "final" else 2
+    for kc in range(n_cvt):
+        for j in range(4):
+            cvt(p, cur, kc, j)
+    p.wait_lds_all()
+    p.emit(f"s_branch {name}_ret_%=")
+
+
 def pipelined_step(p, r, masked_next):
     """Tile j (scores in cur) with the scores of tile j+1 (into nxt)."""
     cur, nxt = (SA, SB) if r % 2 == 0 else (SB, SA)
     st_v, st_k = r % 3, (r + 1) % 3
+    p.valu(f"v_mov_b32 v{T0}, 0", [], [T0])
+    p.valu(f"v_mov_b32 v{T1}, 0", [], [T1])
     # K operands 0, 1 of tile j+1, then four exponentials while they land
     read_k(p, st_k, 0)
     read_k(p, st_k, 1)
@@ -461,13 +554,13 @@ def pipelined_step(p, r, masked_next):
             read_v(p, st_v, f - 6)
         if f < 7:
             exps(p, cur, range(4 + 4 * f, 8 + 4 * f))
+        sums_into(p, cur, range(4 * f, 4 * f + 4))
     for kc in range(2):
         for j in range(4):
             cvt(p, cur, kc, j)
+    rescale_check(p, r, cur, "m" if masked_next else "p")
     if masked_next:
         mask_scores(p, nxt)
-    mops = max_ops(nxt)
-    adds = list(range(32))
     cv = [(kc, j) for kc in (2, 3) for j in range(4)]
     for g in range(8):
         kc, db = g // 2, g % 2
@@ -478,45 +571,35 @@ def pipelined_step(p, r, masked_next):
         for _ in range(2):
             if cv:
                 cvt(p, cur, *cv.pop(0))
-        for _ in range(4):
-            if adds:
-                a = adds.pop(0)
-                lreg = L0 if a % 2 == 0 else L1
-                p.valu(f"v_add_f32 v{lreg}, v{lreg}, v{cur + a}", [lreg, cur + a], [lreg])
-        for _ in range(2):
-            if mops:
-                emit_max_op(p, nxt, mops.pop(0))
-    while mops:
-        emit_max_op(p, nxt, mops.pop(0))
     p.wait_lds_all()
 
 
 def final_step(p, r):
-    """The wave's last tile: exponentials, P V and the row sum; no next tile."""
+    """The wave's last tile: exponentials, the row sum and P V; no next tile."""
     cur = SA if r % 2 == 0 else SB
     st_v = r % 3
+    p.valu(f"v_mov_b32 v{T0}, 0", [], [T0])
+    p.valu(f"v_mov_b32 v{T1}, 0", [], [T1])
     read_v(p, st_v, 0)
     read_v(p, st_v, 1)
     exps(p, cur, range(32))
+    sums_into(p, cur, range(32))
     for kc in range(4):
         for j in range(4):
             cvt(p, cur, kc, j)
-    adds = list(range(32))
+    rescale_check(p, r, cur, "final")
     for g in range(8):
         kc, db = g // 2, g % 2
         p.wait_lds(("v", g))
         p.mfma(ACC + 16 * db, VR + 4 * (g % 2), P + 4 * kc, ACC + 16 * db)
         if g < 6:
             read_v(p, st_v, g + 2)
-        for _ in range(4):
-            a = adds.pop(0)
-            lreg = L0 if a % 2 == 0 else L1
-            p.valu(f"v_add_f32 v{lreg}, v{lreg}, v{cur + a}", [lreg, cur + a], [lreg])
     p.wait_lds_all()
 
 
 def program():
     p = Prog()
+    REDO.clear()
     acc_regs = list(range(ACC, ACC + 32))
     # ---- lane setup (temporaries live in the second score buffer) ----------
     lane = 163
@@ -629,12 +712,10 @@ def program():
         p.emit(f"s_cmp_eq_u32 s{ST0}, %[jlast]")
         p.emit(f"s_cbranch_scc1 fwd_pipem{r}_%=")
         pipelined_step(p, r, False)
-        max_tail(p, f"fwd_resc{r}")
         p.emit(f"s_branch fwd_next{r}_%=")
         p.restore(dispatch)
         p.label(f"fwd_pipem{r}", align=True)
         pipelined_step(p, r, True)
-        max_tail(p, f"fwd_rescm{r}")
         p.emit(f"s_branch fwd_next{r}_%=")
         p.restore(dispatch)
         p.label(f"fwd_final{r}", align=True)
@@ -686,6 +767,11 @@ def program():
     p.valu(f"v_lshlrev_b32 v{T1}, 2, v{e_l32}", [e_l32], [T1])
     p.emit(f"global_store_dword v{T1}, v{T0}, %[lbase]", "vmem", [T1, T0], [])
     p.emit(f"s_mov_b64 exec, s[{SEXEC}:{SEXEC + 1}]")
+    # ---- the rescale blocks, out of line ----------------------------------------
+    p.emit("s_branch fwd_exit_%=")
+    for blk in list(REDO):
+        redo_block(p, *blk)
+    p.label("fwd_exit")
     return p.lines
 
 

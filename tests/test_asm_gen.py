@@ -68,8 +68,13 @@ def test_program_well_formed():
     # one barrier before the first tile and one per step body (6 unrolled steps)
     assert sum(ln == "s_barrier" for ln in lines) == 7
     # 16 MFMAs per pipelined step, two variants per step, plus the first
-    # tile's 8 and the last step's 8 per step
-    assert sum(ln.startswith("v_mfma") for ln in lines) == 8 + 6 * (16 + 16 + 8)
+    # tile's 8 and the last step's 8 per step, and 8 in each of the three
+    # out-of-line rescale blocks per step
+    assert sum(ln.startswith("v_mfma") for ln in lines) == 8 + 6 * (16 + 16 + 8) + 6 * 3 * 8
+    # the rescale blocks sit after the epilogue, hold no barrier and branch back
+    tail = lines[lines.index("s_branch fwd_exit_%="):]
+    assert "s_barrier" not in tail
+    assert sum(ln.startswith("s_branch fwd_redo") for ln in tail) == 18
 
 
 def test_program_hazard_distances_fwd():
