@@ -283,10 +283,17 @@ __global__ __launch_bounds__(256, CATTN_FWD_WAVES_PER_SIMD) void attn_fwd_bf16_k
 // the O and LSE stores. C++ only maps the workgroup to (query tile, head),
 // exactly as above, and hands the program wave-uniform scalars. The program
 // issues one MFMA between every few VALU instructions: the scores of tile
-// j+1 between the exponentials of tile j, P V of tile j between the row sum
-// of j and the row max of j+1. Compiled from the C++ above (build with
-// -DCATTN_FWD_COMPILED), the same schedule waits on each operand read just
-// before its MFMA and runs about 10% slower.
+// j+1 between the exponentials of tile j, P V of tile j beside the row sums
+// of j. It tests the lazy rescale differently from the C++ above: not the
+// next tile's row max against m, but each lane's sum of P over its 32 keys of
+// the tile against 2^8, after the exponentials. A row whose half-row sum
+// passed it (rare after the first tiles) takes an out-of-line block that
+// recomputes the tile's scores, moves m to the running max, rescales and
+// redoes the exponentials; the other rows recompute the same P and scale by
+// exactly 1. Every P used is again at most 2^8, and the common path needs no
+// per-tile row max. Compiled from the C++ above (build with
+// -DCATTN_FWD_COMPILED), the schedule waits on each operand read just before
+// its MFMA and runs about 10% slower.
 #include "attn_fwd_asm.inc"
 
 // One (query tile, head) item: the wave's program from the Q load to the O

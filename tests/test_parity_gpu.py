@@ -117,8 +117,10 @@ def _growing_keys(H, a=16.0, g=1.0 / 16.0):
     """Q_i += a u and K_j += g j u with u = (1/8, ..., 1/8) (a unit vector for
     d = 64), so the logit of key j grows by about a g / 8 = 1/8 per key: the
     running row maximum rises by more than 12 (base 2) on every 64-key tile,
-    above the forward's lazy-rescale threshold of 8, so every tile of every
-    row takes the rescale branch.
+    so P against the stale reference reaches about 2^12, far above the
+    forward's lazy-rescale limit of 2^8 (on a tile's row max in the compiled
+    form, on a tile's half-row sum of P in the hand-scheduled one), and every
+    tile of every row takes the rescale branch.
 
     The ramp sits mostly on the query side on purpose. Each row of dS sums to
     zero, so dQ_i = sum_j dS_ij (K_j - c) for any c, and the bf16 rounding of
