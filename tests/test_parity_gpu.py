@@ -148,6 +148,44 @@ def test_growing_keys_rescale_every_tile(dtype):
                 transform=_growing_keys(2))
 
 
+def _spikes_on_some_rows(H, a=48.0):
+    """Q_i += a u for every fifth query, and K_j += b_j u for every 37th key
+    from key 5 with b_j = 1 + j // 37, u = (1/8, ..., 1/8). A spiked query
+    meets the n-th spiked key with a logit near a n / 8 = 6 n, so each new
+    spiked key lifts that row's logits by about 6 (8.7 base 2) over the ones
+    before it: on the tile that holds it, the row's sum of P against its
+    stale reference passes 2^8, while the other rows of the same wave and
+    the spiked row's other tiles stay below. A spiked key falls in one lane
+    half of the score tile, so many rescales are asked for by one half of the
+    row alone. (A float64 count of the test's sum criterion on these inputs:
+    845 of 6960 row-tiles rescale, 490 of them on one half's sum, and 158
+    wave-tiles mix rows that rescale with rows that do not. A float64
+    emulation of the bf16 rounding of E, P and dS gives 1.4e-2 max-abs on O
+    against the stress bar of 3.2e-2, and 6.9e-3, 8.2e-3, 1.2e-3 relative L2
+    on dQ, dK, dV.) A key-side spike of 6 n with a = 8 instead would put
+    |K| where the bf16 dS rounding alone reaches 2.0e-2 on dQ."""
+    C = H * D
+
+    def fn(x):
+        T = x.shape[1]
+        u = np.float32(1.0 / 8.0)
+        j = np.arange(T)
+        rows = (j % 5 == 0)[None, :, None]
+        keys = (j % 37 == 5)[None, :, None]
+        bj = (1.0 + j // 37).astype(np.float32)[None, :, None]
+        x[..., :C] += np.where(rows, np.float32(a) * u, np.float32(0))
+        x[..., C:2 * C] += np.where(keys, bj * u, np.float32(0))
+        return x
+    return fn
+
+
+def test_spiked_keys_rescale_some_rows():
+    """bf16 only: its logits (up to about 114) lie beyond where the fp32 bar
+    holds for a plain fp32 computation."""
+    _check_case(2, 700, 2, "bf16", 1.0, 0.01, seed=23, label="spiked keys", stress=True,
+                transform=_spikes_on_some_rows(2))
+
+
 def _binade_edge_values(H):
     """V replaced by +-m 2^e with m = 1 or 2 - 2^-7 (the two ends of a bf16
     binade) and e from -24 to 60, chosen from the drawn value itself, so V

@@ -57,6 +57,34 @@ def test_causality_is_bitwise(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causality_is_bitwise_when_later_rows_rescale(dtype):
+    """As above, but the later tokens get Q and K scaled by 8, so their rows
+    take the forward's rescale path on almost every tile while the earlier
+    rows of the same waves (t = 173 falls inside the 32-row wave 160-191)
+    do not: a row that did not ask for a rescale must come out the same."""
+    B, T, H, t = 2, 300, 3, 173
+    C = H * D
+    log(f"[case] causality with rescales {dtype} B={B} T={T} H={H} t={t}")
+    qkv, dout = _inputs(B, T, H, dtype, seed=23)
+    dout_a = dout.copy()
+    dout_a[:, t:] = 0
+    noise = _inputs(B, T, H, dtype, seed=24)[0]
+    x = I.bf16_bits_to_f32(noise) if dtype == "bf16" else noise.copy()
+    x[..., :2 * C] *= np.float32(8.0)  # a power of two: exact in bf16 and f32
+    noise = I.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    qkv_b = qkv.copy()
+    qkv_b[:, t:] = noise[:, t:]
+    ra = run_library(to_device(qkv, dtype), to_device(dout_a, dtype), H)
+    rb = run_library(to_device(qkv_b, dtype), to_device(dout_a, dtype), H)
+    oa, la, ga = (_bits(x) for x in ra)
+    ob, lb, gb = (_bits(x) for x in rb)
+    assert np.array_equal(oa[:, :t], ob[:, :t])
+    assert np.array_equal(la[:, :, :t], lb[:, :, :t])
+    assert np.array_equal(ga[:, :t], gb[:, :t])
+    assert not np.array_equal(oa[:, t:], ob[:, t:])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_runs_are_bitwise_identical(dtype):
     B, T, H = 2, 1000, 3
     log(f"[case] determinism {dtype}")
