@@ -7,11 +7,12 @@ The forward kernel (attn_fwd_bf16.hip) runs this program as one inline-asm
 block per wave: 32 queries of one (batch, head) against 64-key tiles that
 stream through a three-stage LDS ring. Scheduling it by hand is what lets the
 matrix cores, the vector ALU and the LDS work at once: the scores S^T = K Q^T
-of tile j+1 are issued one MFMA at a time between the exponentials of tile j,
-and the P V MFMAs of tile j between the row sum of tile j and the row max of
-tile j+1. Compiled from C++, the same work ran 2.4 times slower per tile
-(each MFMA waited on an LDS read issued just before it, and the phases did not
-overlap).
+of tile j+1 are issued one MFMA at a time between the exponentials and the
+row-sum adds of tile j, and the P V MFMAs of tile j between the conversions of
+its second half. The lazy rescale is tested on each lane's sum of P over the
+tile (against 2^8) and handled out of line. Compiled from C++, the same work
+ran 2.4 times slower per tile (each MFMA waited on an LDS read issued just
+before it, and the phases did not overlap).
 
 The generator tracks the wait states the hardware leaves to software:
   * an MFMA result read (or overwritten) by a non-MFMA instruction: at least
@@ -24,11 +25,12 @@ Where the distance is short it inserts s_nop.
 Register map (VGPR): v0-15 Q^T operands (4 k-steps); v16-47 / v48-79 the two
 score buffers (S^T of a tile as two 32x32 C blocks); v80-87 K operand ring
 (2); v88-95 V^T operand ring (2); v96-111 P^T operands (4); v112-143 O^T
-accumulators (2 d blocks); v144 running max m (base 2, scaled); v145/v146 row
-sum halves; v147 tile max; v148/v149 temporaries; v150 -inf; v151 c (scale *
+accumulators (2 d blocks); v144 reference m (base 2, scaled); v145/v146 row
+sum halves; v147 tile max (first tile and rescale blocks); v148/v149 the
+lane's partial sums of P of the current tile, else temporaries; v150 -inf; v151 c (scale *
 log2 e); v152-155 K read offsets (per k-step); v156-159 V^T read offsets
 (d block, half); v160/161 tile-load offsets; v162 mask limit; v163 lane ^ 32
-byte address for the row max across the lane halves.
+byte address for exchanges across the lane halves.
 """
 
 from __future__ import annotations
